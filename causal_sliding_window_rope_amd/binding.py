@@ -1,0 +1,202 @@
+"""Thin ctypes binding of libswa (the C ABI declared in include/swa.h).
+
+Argument marshalling only: every function takes torch tensors that already live on the GPU,
+checks their dtype / shape / contiguity, and passes raw device pointers plus the current HIP
+stream to the library. All computation happens in the library's HIP kernels. If the library
+is not built, every call raises; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libswa.so")
+
+SWA_F32, SWA_BF16 = 0, 1
+SWA_WINDOW_FULL = -1
+STATUS = {0: "SWA_OK", 1: "SWA_ERR_INVALID_ARG", 2: "SWA_ERR_UNSUPPORTED", 3: "SWA_ERR_ALIGN",
+          4: "SWA_ERR_WORKSPACE", 5: "SWA_ERR_HIP"}
+
+# exported symbol -> (restype, argtypes); must match include/swa.h
+_P, _I, _F, _D, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_double, ctypes.c_size_t
+SIGNATURES = {
+    "swa_last_error": (ctypes.c_char_p, []),
+    "swa_version": (ctypes.c_char_p, []),
+    "rope_table": (_I, [_P, _I, _I, _D, _P]),
+    "rope_qknorm_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
+    "rope_qknorm_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
+    "ve_gate_v": (_I, [_P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "ve_gate_v_bwd": (_I, [_P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "swa_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "swa_bwd_workspace_size": (_S, [_I, _I, _I, _I, _I]),
+    "swa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
+                     _I, _I, _I, _I, _I, _F, _I, _P]),
+}
+
+_lib = None
+
+
+class SwaError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} -> {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libswa.so (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m causal_sliding_window_rope_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    _lib = lib
+    return lib
+
+
+def _call(name: str, *args) -> int:
+    lib = load()
+    st = getattr(lib, name)(*args)
+    if st != 0:
+        raise SwaError(name, st, lib.swa_last_error().decode())
+    return st
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SWA_BF16
+    if t.dtype == torch.float32:
+        return SWA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check(t: torch.Tensor, name: str, shape=None, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def version() -> str:
+    return load().swa_version().decode()
+
+
+def rope_table(T: int, D: int, base: float = 10000.0, device="cuda") -> torch.Tensor:
+    cs = torch.empty((T, D // 2, 2), dtype=torch.float32, device=device)
+    _call("rope_table", _ptr(cs), T, D, float(base), _stream())
+    return cs
+
+
+def rope_qknorm_fwd(q, k, cos_sin, eps: float = 1e-6):
+    B, T, H, D = q.shape
+    for t, n in ((q, "q"), (k, "k")):
+        _check(t, n, (B, T, H, D), q.dtype)
+    _check(cos_sin, "cos_sin", (T, D // 2, 2), torch.float32)
+    qn, kn = torch.empty_like(q), torch.empty_like(k)
+    _call("rope_qknorm_fwd", _ptr(q), _ptr(k), _ptr(cos_sin), _ptr(qn), _ptr(kn), B, T, H, D,
+          float(eps), _dt(q), _stream())
+    return qn, kn
+
+
+def rope_qknorm_bwd(q, k, cos_sin, dqn, dkn, eps: float = 1e-6):
+    B, T, H, D = q.shape
+    for t, n in ((q, "q"), (k, "k"), (dqn, "dqn"), (dkn, "dkn")):
+        _check(t, n, (B, T, H, D), q.dtype)
+    _check(cos_sin, "cos_sin", (T, D // 2, 2), torch.float32)
+    dq, dk = torch.empty_like(q), torch.empty_like(k)
+    _call("rope_qknorm_bwd", _ptr(q), _ptr(k), _ptr(cos_sin), _ptr(dqn), _ptr(dkn), _ptr(dq),
+          _ptr(dk), B, T, H, D, float(eps), _dt(q), _stream())
+    return dq, dk
+
+
+def ve_gate_v(x, Wg, v=None, ve=None, materialize: bool = False):
+    """gate (B, T, H) float32; with materialize=True also v_eff = v + gate * ve."""
+    B, T, C = x.shape
+    H = Wg.shape[1]
+    _check(x, "x")
+    _check(Wg, "Wg", (32, H), torch.float32)
+    gate = torch.empty((B, T, H), dtype=torch.float32, device=x.device)
+    D = v.shape[-1] if v is not None else 64
+    v_eff = torch.empty_like(v) if materialize else None
+    _call("ve_gate_v", _ptr(x), C, _ptr(Wg), _ptr(gate), _ptr(v if materialize else None),
+          _ptr(ve if materialize else None), _ptr(v_eff), B, T, H, D, _dt(x), _stream())
+    return (gate, v_eff) if materialize else gate
+
+
+def ve_gate_v_bwd(x, Wg, gate, dgate, want_dx32: bool = True):
+    B, T, C = x.shape
+    H = Wg.shape[1]
+    _check(x, "x")
+    _check(gate, "gate", (B, T, H), torch.float32)
+    _check(dgate, "dgate", (B, T, H), torch.float32)
+    dWg = torch.empty((32, H), dtype=torch.float32, device=x.device)
+    dx32 = torch.empty((B, T, 32), dtype=x.dtype, device=x.device) if want_dx32 else None
+    _call("ve_gate_v_bwd", _ptr(x), C, _ptr(Wg), _ptr(gate), _ptr(dgate), _ptr(dWg), _ptr(dx32),
+          B, T, H, _dt(x), _stream())
+    return dWg, dx32
+
+
+def swa_fwd(q, k, v, window: int, scale: float | None = None, ve=None, gate=None, out=None,
+            lse=None):
+    B, T, H, D = q.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, (B, T, H, D), q.dtype)
+    if ve is not None:
+        _check(ve, "ve", (B, T, H * D), q.dtype)
+        _check(gate, "gate", (B, T, H), torch.float32)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if lse is None else lse
+    _call("swa_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), _ptr(o), _ptr(lse), B, T, H,
+          D, int(window), float(scale), _dt(q), _stream())
+    return o, lse
+
+
+def swa_bwd_workspace_size(B: int, T: int, H: int, D: int, dtype: torch.dtype) -> int:
+    return load().swa_bwd_workspace_size(B, T, H, D, SWA_BF16 if dtype == torch.bfloat16 else SWA_F32)
+
+
+def swa_bwd(q, k, v, o, lse, dO, window: int, scale: float | None = None, ve=None, gate=None,
+            workspace=None, grads=None):
+    """Returns (dq, dk, dv) or, with the gate, (dq, dk, dv, dve, dgate)."""
+    B, T, H, D = q.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dO, "dO")):
+        _check(t, n, (B, T, H, D), q.dtype)
+    _check(lse, "lse", (B, H, T), torch.float32)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    ws_bytes = swa_bwd_workspace_size(B, T, H, D, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    if grads is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dve = torch.empty_like(ve) if ve is not None else None
+        dgate = torch.empty((B, T, H), dtype=torch.float32, device=q.device) if ve is not None else None
+    else:
+        dq, dk, dv, dve, dgate = grads
+    _call("swa_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), _ptr(o), _ptr(lse), _ptr(dO),
+          _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dve), _ptr(dgate), _ptr(workspace),
+          workspace.numel() * workspace.element_size(), B, T, H, D, int(window), float(scale),
+          _dt(q), _stream())
+    if ve is not None:
+        return dq, dk, dv, dve, dgate
+    return dq, dk, dv

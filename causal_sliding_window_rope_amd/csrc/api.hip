@@ -1,0 +1,200 @@
+// C ABI of libswa: argument validation on the host, then kernel dispatch on the caller's stream.
+// Declarations and the contract of every entry point are in include/swa.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/swa.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return SWA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SWA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shared checks of (B, T, H, D, dtype); returns 0 or a status with the message set.
+int check_shape(const char* fn, int B, int T, int H, int D, int dtype) {
+  if (B < 1 || T < 1 || H < 1)
+    return fail(SWA_ERR_INVALID_ARG, "%s: B, T, H must be >= 1 (got %d, %d, %d)", fn, B, T, H);
+  if (dtype != SWA_F32 && dtype != SWA_BF16)
+    return fail(SWA_ERR_INVALID_ARG, "%s: dtype must be SWA_F32 or SWA_BF16 (got %d)", fn, dtype);
+  if (D != 64 && D != 128)
+    return fail(SWA_ERR_UNSUPPORTED, "%s: head dim D must be 64 or 128 (got %d)", fn, D);
+  const long long n = (long long)B * T * H * D;
+  if (n >= (1LL << 31) / 2 || (long long)B * H * T >= (1LL << 31) / 2)
+    return fail(SWA_ERR_UNSUPPORTED, "%s: B*T*H*D = %lld exceeds the supported index range", fn, n);
+  return 0;
+}
+
+int need(const char* fn, const char* name, const void* p) {
+  if (!p) return fail(SWA_ERR_INVALID_ARG, "%s: %s must not be NULL", fn, name);
+  if (!aligned16(p)) return fail(SWA_ERR_ALIGN, "%s: %s must be 16-byte aligned", fn, name);
+  return 0;
+}
+
+int opt(const char* fn, const char* name, const void* p) {
+  if (p && !aligned16(p)) return fail(SWA_ERR_ALIGN, "%s: %s must be 16-byte aligned", fn, name);
+  return 0;
+}
+
+int check_window_scale(const char* fn, int window, float scale, int T, int* w_out) {
+  if (window == 0 || window < SWA_WINDOW_FULL)
+    return fail(SWA_ERR_INVALID_ARG, "%s: window must be >= 1 or SWA_WINDOW_FULL (got %d)", fn,
+                window);
+  if (!(std::isfinite(scale) && scale > 0.f))
+    return fail(SWA_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
+  *w_out = (window == SWA_WINDOW_FULL || window > T) ? T : window;
+  return 0;
+}
+
+}  // namespace
+
+#define SWA_TRY(expr)        \
+  do {                       \
+    int _st = (expr);        \
+    if (_st) return _st;     \
+  } while (0)
+
+extern "C" {
+
+const char* swa_last_error(void) { return g_last_error.c_str(); }
+
+const char* swa_version(void) { return "swa 1.0 gfx950"; }
+
+int rope_table(float* cos_sin, int T, int D, double base, void* stream) {
+  const char* fn = "rope_table";
+  SWA_TRY(need(fn, "cos_sin", cos_sin));
+  if (T < 1) return fail(SWA_ERR_INVALID_ARG, "%s: T must be >= 1", fn);
+  if (D != 64 && D != 128) return fail(SWA_ERR_UNSUPPORTED, "%s: D must be 64 or 128", fn);
+  if (!(std::isfinite(base) && base > 0.0))
+    return fail(SWA_ERR_INVALID_ARG, "%s: base must be finite and > 0", fn);
+  return hip_status(swa::launch_rope_table(cos_sin, T, D, base, (hipStream_t)stream), fn);
+}
+
+int rope_qknorm_fwd(const void* q, const void* k, const float* cos_sin, void* qn, void* kn, int B,
+                    int T, int H, int D, float eps, swa_dtype dtype, void* stream) {
+  const char* fn = "rope_qknorm_fwd";
+  SWA_TRY(check_shape(fn, B, T, H, D, dtype));
+  SWA_TRY(need(fn, "q", q)); SWA_TRY(need(fn, "k", k)); SWA_TRY(need(fn, "cos_sin", cos_sin));
+  SWA_TRY(need(fn, "qn", qn)); SWA_TRY(need(fn, "kn", kn));
+  if (!(std::isfinite(eps) && eps >= 0.f))
+    return fail(SWA_ERR_INVALID_ARG, "%s: eps must be finite and >= 0", fn);
+  if (qn == q || qn == k || kn == q || kn == k)
+    return fail(SWA_ERR_INVALID_ARG, "%s: outputs may not alias inputs", fn);
+  return hip_status(swa::launch_rope_qknorm_fwd(q, k, cos_sin, qn, kn, B, T, H, D, eps,
+                                                dtype == SWA_BF16, (hipStream_t)stream), fn);
+}
+
+int rope_qknorm_bwd(const void* q, const void* k, const float* cos_sin, const void* dqn,
+                    const void* dkn, void* dq, void* dk, int B, int T, int H, int D, float eps,
+                    swa_dtype dtype, void* stream) {
+  const char* fn = "rope_qknorm_bwd";
+  SWA_TRY(check_shape(fn, B, T, H, D, dtype));
+  SWA_TRY(need(fn, "q", q)); SWA_TRY(need(fn, "k", k)); SWA_TRY(need(fn, "cos_sin", cos_sin));
+  SWA_TRY(need(fn, "dqn", dqn)); SWA_TRY(need(fn, "dkn", dkn));
+  SWA_TRY(need(fn, "dq", dq)); SWA_TRY(need(fn, "dk", dk));
+  if (!(std::isfinite(eps) && eps >= 0.f))
+    return fail(SWA_ERR_INVALID_ARG, "%s: eps must be finite and >= 0", fn);
+  return hip_status(swa::launch_rope_qknorm_bwd(q, k, cos_sin, dqn, dkn, dq, dk, B, T, H, D, eps,
+                                                dtype == SWA_BF16, (hipStream_t)stream), fn);
+}
+
+int ve_gate_v(const void* x, int ldx, const float* Wg, float* gate, const void* v, const void* ve,
+              void* v_eff, int B, int T, int H, int D, swa_dtype dtype, void* stream) {
+  const char* fn = "ve_gate_v";
+  SWA_TRY(check_shape(fn, B, T, H, D, dtype));
+  if (!x || !Wg || !gate) return fail(SWA_ERR_INVALID_ARG, "%s: x, Wg and gate are required", fn);
+  if (ldx < SWA_GATE_CHANNELS) return fail(SWA_ERR_INVALID_ARG, "%s: ldx must be >= 32", fn);
+  const int nset = (v != nullptr) + (ve != nullptr) + (v_eff != nullptr);
+  if (nset != 0 && nset != 3)
+    return fail(SWA_ERR_INVALID_ARG, "%s: v, ve, v_eff must be all set or all NULL", fn);
+  if (nset == 3) { SWA_TRY(need(fn, "v", v)); SWA_TRY(need(fn, "ve", ve)); SWA_TRY(need(fn, "v_eff", v_eff)); }
+  return hip_status(swa::launch_ve_gate(x, ldx, Wg, gate, v, ve, v_eff, B, T, H, D,
+                                        dtype == SWA_BF16, (hipStream_t)stream), fn);
+}
+
+int ve_gate_v_bwd(const void* x, int ldx, const float* Wg, const float* gate, const float* dgate,
+                  float* dWg, void* dx32, int B, int T, int H, swa_dtype dtype, void* stream) {
+  const char* fn = "ve_gate_v_bwd";
+  SWA_TRY(check_shape(fn, B, T, H, 64, dtype));
+  if (!x || !Wg || !gate || !dgate || !dWg)
+    return fail(SWA_ERR_INVALID_ARG, "%s: x, Wg, gate, dgate and dWg are required", fn);
+  if (ldx < SWA_GATE_CHANNELS) return fail(SWA_ERR_INVALID_ARG, "%s: ldx must be >= 32", fn);
+  return hip_status(swa::launch_ve_gate_bwd(x, ldx, Wg, gate, dgate, dWg, dx32, B, T, H,
+                                            dtype == SWA_BF16, (hipStream_t)stream), fn);
+}
+
+int swa_fwd(const void* q, const void* k, const void* v, const void* ve, const float* gate, void* o,
+            float* lse, int B, int T, int H, int D, int window, float scale, swa_dtype dtype,
+            void* stream) {
+  const char* fn = "swa_fwd";
+  SWA_TRY(check_shape(fn, B, T, H, D, dtype));
+  SWA_TRY(need(fn, "q", q)); SWA_TRY(need(fn, "k", k)); SWA_TRY(need(fn, "v", v));
+  SWA_TRY(need(fn, "o", o)); SWA_TRY(need(fn, "lse", lse));
+  if ((ve == nullptr) != (gate == nullptr))
+    return fail(SWA_ERR_INVALID_ARG, "%s: ve and gate must be given together", fn);
+  SWA_TRY(opt(fn, "ve", ve));
+  swa::AttnShape a{B, T, H, D, 0, scale};
+  SWA_TRY(check_window_scale(fn, window, scale, T, &a.window));
+  return hip_status(swa::launch_fwd(a, q, k, v, ve, gate, o, lse, dtype == SWA_BF16,
+                                    (hipStream_t)stream), fn);
+}
+
+size_t swa_bwd_workspace_size(int B, int T, int H, int D, swa_dtype dtype) {
+  if (B < 1 || T < 1 || H < 1 || (D != 64 && D != 128)) return 0;
+  return swa::bwd_workspace_bytes(B, T, H, D, dtype == SWA_BF16);
+}
+
+int swa_bwd(const void* q, const void* k, const void* v, const void* ve, const float* gate,
+            const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
+            void* dve, float* dgate, void* workspace, size_t ws_bytes, int B, int T, int H, int D,
+            int window, float scale, swa_dtype dtype, void* stream) {
+  const char* fn = "swa_bwd";
+  SWA_TRY(check_shape(fn, B, T, H, D, dtype));
+  SWA_TRY(need(fn, "q", q)); SWA_TRY(need(fn, "k", k)); SWA_TRY(need(fn, "v", v));
+  SWA_TRY(need(fn, "o", o)); SWA_TRY(need(fn, "lse", lse)); SWA_TRY(need(fn, "dO", dO));
+  SWA_TRY(need(fn, "dq", dq)); SWA_TRY(need(fn, "dk", dk)); SWA_TRY(need(fn, "dv", dv));
+  const bool g = gate != nullptr;
+  if ((ve != nullptr) != g)
+    return fail(SWA_ERR_INVALID_ARG, "%s: ve and gate must be given together", fn);
+  if (g != (dve != nullptr) || g != (dgate != nullptr))
+    return fail(SWA_ERR_INVALID_ARG, "%s: dve and dgate are required with the gate, NULL without", fn);
+  SWA_TRY(opt(fn, "ve", ve)); SWA_TRY(opt(fn, "dve", dve));
+  swa::AttnShape a{B, T, H, D, 0, scale};
+  SWA_TRY(check_window_scale(fn, window, scale, T, &a.window));
+  const size_t need_ws = swa::bwd_workspace_bytes(B, T, H, D, dtype == SWA_BF16);
+  if (!workspace || ws_bytes < need_ws)
+    return fail(SWA_ERR_WORKSPACE, "%s: workspace of %zu bytes required (got %zu)", fn, need_ws,
+                workspace ? ws_bytes : (size_t)0);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(SWA_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+  return hip_status(swa::launch_bwd(a, q, k, v, ve, gate, o, lse, dO, dq, dk, dv, dve, dgate,
+                                    workspace, dtype == SWA_BF16, (hipStream_t)stream), fn);
+}
+
+}  // extern "C"

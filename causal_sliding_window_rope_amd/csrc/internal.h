@@ -1,0 +1,39 @@
+// Host-side launchers of the libswa kernels (called by the C ABI in api.hip after validation).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace swa {
+
+struct AttnShape {
+  int B, T, H, D;
+  int window;   // already clamped: 1 <= window <= T
+  float scale;
+};
+
+hipError_t launch_rope_table(float* cos_sin, int T, int D, double base, hipStream_t s);
+hipError_t launch_rope_qknorm_fwd(const void* q, const void* k, const float* cs, void* qn, void* kn,
+                                  int B, int T, int H, int D, float eps, bool bf16, hipStream_t s);
+hipError_t launch_rope_qknorm_bwd(const void* q, const void* k, const float* cs, const void* dqn,
+                                  const void* dkn, void* dq, void* dk, int B, int T, int H, int D,
+                                  float eps, bool bf16, hipStream_t s);
+
+hipError_t launch_ve_gate(const void* x, int ldx, const float* Wg, float* gate, const void* v,
+                          const void* ve, void* v_eff, int B, int T, int H, int D, bool bf16,
+                          hipStream_t s);
+hipError_t launch_ve_gate_bwd(const void* x, int ldx, const float* Wg, const float* gate,
+                              const float* dgate, float* dWg, void* dx32, int B, int T, int H,
+                              bool bf16, hipStream_t s);
+
+hipError_t launch_fwd(const AttnShape& a, const void* q, const void* k, const void* v,
+                      const void* ve, const float* gate, void* o, float* lse, bool bf16,
+                      hipStream_t s);
+
+size_t bwd_workspace_bytes(int B, int T, int H, int D, bool bf16);
+hipError_t launch_bwd(const AttnShape& a, const void* q, const void* k, const void* v,
+                      const void* ve, const float* gate, const void* o, const float* lse,
+                      const void* dO, void* dq, void* dk, void* dv, void* dve, float* dgate,
+                      void* ws, bool bf16, hipStream_t s);
+
+}  // namespace swa

@@ -1,0 +1,217 @@
+// RoPE table and the fused RoPE -> RMS QK-norm prologue (forward and backward) for gfx950.
+//
+// "从4万美元到73美元：GPT-2复现的成本革命" (intelliparadigm.com) §2.2: q, k = norm(rope(q)),
+// norm(rope(k)); §2.1: the RMSNorm has no learnable parameters. The rotation is rotate-half:
+// pair (i, i + D/2) turns by t * theta_i, theta_i = base^(-2i/D).
+//
+// These kernels are HBM-bound: one row of D elements per (tensor, b, t, h) is read once and
+// written once. A row is spread over D*sizeof(E)/16 lanes so that every lane moves exactly one
+// 128-bit word; the rotation partner of lane j is lane j ^ (lanes/2) (a DPP/permute within
+// the row's lane group) and the row sum of squares is a butterfly over the same group.
+#include "common.h"
+#include "internal.h"
+
+namespace swa {
+
+__global__ void __launch_bounds__(256) rope_table_kernel(float* __restrict__ cs, int T, int D,
+                                                         double base) {
+  const int half = D / 2;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= T * half) return;
+  const int t = idx / half, i = idx - t * half;
+  const double theta = pow(base, -2.0 * (double)i / (double)D);
+  const double ang = (double)t * theta;
+  cs[2 * idx + 0] = (float)cos(ang);
+  cs[2 * idx + 1] = (float)sin(ang);
+}
+
+hipError_t launch_rope_table(float* cos_sin, int T, int D, double base, hipStream_t s) {
+  const int n = T * (D / 2);
+  hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, s, cos_sin, T, D,
+                     base);
+  return hipGetLastError();
+}
+
+// One 128-bit word of a row: VPT elements as floats.
+template <typename E> struct RowWord {
+  static constexpr int VPT = 16 / sizeof(E);
+  float v[VPT];
+  __device__ __forceinline__ void load(const E* p) {
+    const uint4 w = *reinterpret_cast<const uint4*>(p);
+    if constexpr (sizeof(E) == 4) {
+      v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y);
+      v[2] = __uint_as_float(w.z); v[3] = __uint_as_float(w.w);
+    } else {
+      v[0] = bf_lo(w.x); v[1] = bf_hi(w.x); v[2] = bf_lo(w.y); v[3] = bf_hi(w.y);
+      v[4] = bf_lo(w.z); v[5] = bf_hi(w.z); v[6] = bf_lo(w.w); v[7] = bf_hi(w.w);
+    }
+  }
+  __device__ __forceinline__ void store(E* p) const {
+    uint4 w;
+    if constexpr (sizeof(E) == 4) {
+      w.x = __float_as_uint(v[0]); w.y = __float_as_uint(v[1]);
+      w.z = __float_as_uint(v[2]); w.w = __float_as_uint(v[3]);
+    } else {
+      w.x = pack_bf2(v[0], v[1]); w.y = pack_bf2(v[2], v[3]);
+      w.z = pack_bf2(v[4], v[5]); w.w = pack_bf2(v[6], v[7]);
+    }
+    *reinterpret_cast<uint4*>(p) = w;
+  }
+};
+
+// Sum over the TPR lanes that hold one row (TPR is a power of two <= 64, groups aligned).
+template <int TPR>
+__device__ __forceinline__ float row_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < TPR; m <<= 1) x += xor_shfl(x, m);
+  return x;
+}
+
+// cos/sin of the VPT angle slots starting at pair index i0 for position t.
+template <int VPT>
+__device__ __forceinline__ void load_cs(const float* __restrict__ cs, int t, int half, int i0,
+                                        float* c, float* s) {
+  const float4* p = reinterpret_cast<const float4*>(cs + 2 * ((size_t)t * half + i0));
+#pragma unroll
+  for (int e = 0; e < VPT / 2; ++e) {
+    const float4 w = p[e];
+    c[2 * e] = w.x; s[2 * e] = w.y; c[2 * e + 1] = w.z; s[2 * e + 1] = w.w;
+  }
+}
+
+// Rotate one word: lanes in the first half of the row hold x1 (pair index i < D/2), lanes in
+// the second half hold x2; `other` is the partner lane's word. sign = +1 forward, -1 transpose.
+template <int VPT>
+__device__ __forceinline__ void rotate(float* y, const float* x, const float* other, const float* c,
+                                       const float* s, bool second_half, float sign) {
+#pragma unroll
+  for (int e = 0; e < VPT; ++e) {
+    const float ss = sign * s[e];
+    // first half: y1 = x1 c - x2 s ; second half: y2 = x1 s + x2 c
+    y[e] = second_half ? fmaf(other[e], ss, x[e] * c[e]) : fmaf(-other[e], ss, x[e] * c[e]);
+  }
+}
+
+template <typename E, int D>
+__global__ void __launch_bounds__(256) rope_qknorm_fwd_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const float* __restrict__ cs,
+    E* __restrict__ qn, E* __restrict__ kn, int rows_per_tensor, int T, int H, float eps) {
+  using W = RowWord<E>;
+  constexpr int VPT = W::VPT, TPR = D / VPT, HALF_T = TPR / 2;
+  const int lane_in_row = threadIdx.x % TPR;
+  const int row = blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  if (row >= 2 * rows_per_tensor) return;  // whole row groups exit together
+  const bool is_k = row >= rows_per_tensor;
+  const int r = is_k ? row - rows_per_tensor : row;
+  const int t = (r / H) % T;
+  const size_t off = (size_t)r * D + lane_in_row * VPT;
+  W x;
+  x.load((is_k ? k : q) + off);
+  const bool second = lane_in_row >= HALF_T;
+  float c[VPT], s[VPT], other[VPT], y[VPT];
+  load_cs<VPT>(cs, t, D / 2, (lane_in_row % HALF_T) * VPT, c, s);
+#pragma unroll
+  for (int e = 0; e < VPT; ++e) other[e] = xor_shfl(x.v[e], HALF_T);
+  rotate<VPT>(y, x.v, other, c, s, second, 1.0f);
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < VPT; ++e) ss = fmaf(y[e], y[e], ss);
+  ss = row_sum<TPR>(ss);
+  const float rinv = 1.0f / sqrtf(ss / (float)D + eps);
+  W out;
+#pragma unroll
+  for (int e = 0; e < VPT; ++e) out.v[e] = y[e] * rinv;
+  out.store((is_k ? kn : qn) + off);
+}
+
+template <typename E, int D>
+__global__ void __launch_bounds__(256) rope_qknorm_bwd_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const float* __restrict__ cs,
+    const E* __restrict__ dqn, const E* __restrict__ dkn, E* __restrict__ dq, E* __restrict__ dk,
+    int rows_per_tensor, int T, int H, float eps) {
+  using W = RowWord<E>;
+  constexpr int VPT = W::VPT, TPR = D / VPT, HALF_T = TPR / 2;
+  const int lane_in_row = threadIdx.x % TPR;
+  const int row = blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  if (row >= 2 * rows_per_tensor) return;
+  const bool is_k = row >= rows_per_tensor;
+  const int r = is_k ? row - rows_per_tensor : row;
+  const int t = (r / H) % T;
+  const size_t off = (size_t)r * D + lane_in_row * VPT;
+  W x, g;
+  x.load((is_k ? k : q) + off);
+  g.load((is_k ? dkn : dqn) + off);
+  const bool second = lane_in_row >= HALF_T;
+  float c[VPT], s[VPT], other[VPT], u[VPT];
+  load_cs<VPT>(cs, t, D / 2, (lane_in_row % HALF_T) * VPT, c, s);
+#pragma unroll
+  for (int e = 0; e < VPT; ++e) other[e] = xor_shfl(x.v[e], HALF_T);
+  rotate<VPT>(u, x.v, other, c, s, second, 1.0f);
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < VPT; ++e) ss = fmaf(u[e], u[e], ss);
+  ss = row_sum<TPR>(ss);
+  const float rinv = 1.0f / sqrtf(ss / (float)D + eps);
+  float dot = 0.f;
+#pragma unroll
+  for (int e = 0; e < VPT; ++e) dot = fmaf(u[e] * rinv, g.v[e], dot);
+  dot = row_sum<TPR>(dot);
+  const float dd = dot / (float)D;
+  float du[VPT];
+#pragma unroll
+  for (int e = 0; e < VPT; ++e) du[e] = rinv * (g.v[e] - u[e] * rinv * dd);
+#pragma unroll
+  for (int e = 0; e < VPT; ++e) other[e] = xor_shfl(du[e], HALF_T);
+  W out;
+  rotate<VPT>(out.v, du, other, c, s, second, -1.0f);
+  out.store((is_k ? dk : dq) + off);
+}
+
+template <typename E, int D>
+static hipError_t launch_fwd_t(const void* q, const void* k, const float* cs, void* qn, void* kn,
+                               int B, int T, int H, float eps, hipStream_t s) {
+  constexpr int TPR = D / (16 / sizeof(E));
+  const int rows = B * T * H;
+  const int rpb = 256 / TPR;
+  const int blocks = (2 * rows + rpb - 1) / rpb;
+  hipLaunchKernelGGL((rope_qknorm_fwd_kernel<E, D>), dim3(blocks), dim3(256), 0, s,
+                     (const E*)q, (const E*)k, cs, (E*)qn, (E*)kn, rows, T, H, eps);
+  return hipGetLastError();
+}
+
+template <typename E, int D>
+static hipError_t launch_bwd_t(const void* q, const void* k, const float* cs, const void* dqn,
+                               const void* dkn, void* dq, void* dk, int B, int T, int H, float eps,
+                               hipStream_t s) {
+  constexpr int TPR = D / (16 / sizeof(E));
+  const int rows = B * T * H;
+  const int rpb = 256 / TPR;
+  const int blocks = (2 * rows + rpb - 1) / rpb;
+  hipLaunchKernelGGL((rope_qknorm_bwd_kernel<E, D>), dim3(blocks), dim3(256), 0, s,
+                     (const E*)q, (const E*)k, cs, (const E*)dqn, (const E*)dkn, (E*)dq, (E*)dk,
+                     rows, T, H, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_qknorm_fwd(const void* q, const void* k, const float* cs, void* qn, void* kn,
+                                  int B, int T, int H, int D, float eps, bool bf16, hipStream_t s) {
+  if (bf16) {
+    return D == 64 ? launch_fwd_t<swa::bf16, 64>(q, k, cs, qn, kn, B, T, H, eps, s)
+                   : launch_fwd_t<swa::bf16, 128>(q, k, cs, qn, kn, B, T, H, eps, s);
+  }
+  return D == 64 ? launch_fwd_t<float, 64>(q, k, cs, qn, kn, B, T, H, eps, s)
+                 : launch_fwd_t<float, 128>(q, k, cs, qn, kn, B, T, H, eps, s);
+}
+
+hipError_t launch_rope_qknorm_bwd(const void* q, const void* k, const float* cs, const void* dqn,
+                                  const void* dkn, void* dq, void* dk, int B, int T, int H, int D,
+                                  float eps, bool bf16, hipStream_t s) {
+  if (bf16) {
+    return D == 64 ? launch_bwd_t<swa::bf16, 64>(q, k, cs, dqn, dkn, dq, dk, B, T, H, eps, s)
+                   : launch_bwd_t<swa::bf16, 128>(q, k, cs, dqn, dkn, dq, dk, B, T, H, eps, s);
+  }
+  return D == 64 ? launch_bwd_t<float, 64>(q, k, cs, dqn, dkn, dq, dk, B, T, H, eps, s)
+                 : launch_bwd_t<float, 128>(q, k, cs, dqn, dkn, dq, dk, B, T, H, eps, s);
+}
+
+}  // namespace swa

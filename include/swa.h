@@ -1,0 +1,166 @@
+/*
+ * swa.h — C ABI of the MI355X (gfx950) causal sliding-window attention library (libswa.so).
+ *
+ * What it computes (the attention core of the nanochat / nanoGPT GPT-2 training step):
+ *
+ *   prologue   q_hat = RMSNorm(RoPE(q)), k_hat = RMSNorm(RoPE(k))
+ *              ("从4万美元到73美元：GPT-2复现的成本革命", intelliparadigm.com, §2.2: q and k are
+ *              normalised after RoPE; §2.1: the norm has no learnable gamma/beta)
+ *   gate       v_eff = v + 2*sigmoid(x[:, :, :32] @ Wg) * ve   (optional; lanjinlin.com.cn
+ *              repost of the same write-up, "3. Value Embeddings")
+ *   attention  s_ij = scale * q_hat_i . k_hat_j for max(0, i-W+1) <= j <= i, softmax over j,
+ *              O_i = sum_j P_ij v_eff_j, lse_i = log sum_j exp(s_ij)
+ *              ("GPT-2 124M 复现", notes.cassieliang.com, §3: scaled dot product, causal
+ *              lower-triangular mask including the diagonal, softmax over keys; §19: tiled
+ *              online softmax, exact, backward by recomputation; intelliparadigm.com §3.2:
+ *              per-layer windows of 1024 or 2048 tokens)
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are device pointers to contiguous arrays in the native (B, T, H, D) layout
+ *     ("从4万美元到73美元" §3.1): element (b, t, h, d) at ((b*T + t)*H + h)*D + d.
+ *     lse and delta are (B, H, T); gate and dgate are (B, T, H); ve is (B, T, H*D) with
+ *     channel h*D + d feeding head h; x is (B, T, ldx) of which channels 0..31 are read.
+ *   - Positions are 0..T-1 in every sequence b; sequences never attend to one another.
+ *   - dtype selects the storage type of q, k, v, o, dO, dq, dk, dv, ve, dve, x and dx32:
+ *     SWA_F32 (float) or SWA_BF16 (bfloat16). lse, gate, dgate, Wg, dWg, cos_sin and the
+ *     workspace are always float32. Arithmetic is float32; the bf16 attention contractions
+ *     run on bf16 MFMA with float32 accumulation.
+ *   - Head dim D must be 64 or 128. window W >= 1 counts keys including the query itself;
+ *     W >= T or W == SWA_WINDOW_FULL is plain causal attention.
+ *   - Ownership: the caller allocates and owns every buffer, including workspaces sized by
+ *     the *_workspace_size queries. The library allocates no device memory and keeps no
+ *     state between calls beyond the thread-local error message.
+ *   - Execution: work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and never synchronised. Outputs are valid once the stream has reached that point.
+ *   - Errors: every call validates all arguments on the host before any launch and returns
+ *     a swa_status; on a non-zero status nothing was enqueued (except SWA_ERR_HIP, where a
+ *     launch failed) and swa_last_error() describes the problem. No C++ exception crosses
+ *     the ABI. Device pointers must be 16-byte aligned (128-bit vector access).
+ *   - Gradients are overwritten, never accumulated into.
+ */
+#ifndef SWA_H_
+#define SWA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SWA_F32 = 0, SWA_BF16 = 1 } swa_dtype;
+
+typedef enum {
+  SWA_OK = 0,
+  SWA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad window/scale/eps/dtype */
+  SWA_ERR_UNSUPPORTED = 2, /* D not 64 or 128, sizes beyond 32-bit index range */
+  SWA_ERR_ALIGN = 3,       /* a device pointer is not 16-byte aligned */
+  SWA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than the query returns */
+  SWA_ERR_HIP = 5          /* a kernel launch failed (message has the HIP error string) */
+} swa_status;
+
+#define SWA_WINDOW_FULL (-1)
+#define SWA_GATE_CHANNELS 32
+
+/* Text of the last non-zero status returned on the calling thread ("" if none). */
+const char* swa_last_error(void);
+
+/* Library version string, e.g. "swa 1.0 gfx950". */
+const char* swa_version(void);
+
+/*
+ * rope_table — RoPE angle table (setup; once per (T, D, base)).
+ * Writes cos_sin[(t*(D/2) + i)*2 + 0] = cos(t*theta_i), [...+1] = sin(t*theta_i) with
+ * theta_i = base^(-2i/D), i < D/2, t < T; angles are formed and evaluated in float64 and
+ * stored as float32. The rotation convention ("NanoGPT Speedrun：大模型训练效率的极限竞速指南",
+ * kongchang.com, "模型架构层面的改进": a position-dependent rotation of q and k; the pages
+ * give no formula) is rotate-half: pair (i, i + D/2) turns by +t*theta_i.
+ *   cos_sin: device, T*D floats, written.   T >= 1, D in {64, 128}, base > 0 finite.
+ */
+int rope_table(float* cos_sin, int T, int D, double base, void* stream);
+
+/*
+ * rope_qknorm_fwd — fused prologue for q and k in one launch
+ * ("从4万美元到73美元" §2.2, §2.1):
+ *   u = RoPE_t(x) over all D dims;  x_hat = u / sqrt(mean_d u^2 + eps).
+ * The 1/sqrt(D) score scale is not applied here; swa_fwd/swa_bwd take it as `scale`.
+ *   q, k   : device (B,T,H,D) dtype, read.         qn, kn: device (B,T,H,D) dtype, written.
+ *   cos_sin: device table from rope_table(T, D).   eps >= 0 finite.
+ * qn/kn may not alias q/k.
+ */
+int rope_qknorm_fwd(const void* q, const void* k, const float* cos_sin, void* qn, void* kn,
+                    int B, int T, int H, int D, float eps, swa_dtype dtype, void* stream);
+
+/*
+ * rope_qknorm_bwd — backward of the prologue, for q and k in one launch.
+ * Recomputes u and r = (mean u^2 + eps)^(-1/2) from the raw input, then
+ *   du = r * (dx_hat - x_hat * (x_hat . dx_hat) / D);   dx = RoPE_t^T(du) (rotation by -t*theta).
+ *   q, k  : device (B,T,H,D) dtype, the raw pre-RoPE inputs, read.
+ *   dqn, dkn: device (B,T,H,D) dtype, gradients w.r.t. q_hat, k_hat, read.
+ *   dq, dk: device (B,T,H,D) dtype, written (may alias dqn/dkn).
+ */
+int rope_qknorm_bwd(const void* q, const void* k, const float* cos_sin, const void* dqn,
+                    const void* dkn, void* dq, void* dk, int B, int T, int H, int D, float eps,
+                    swa_dtype dtype, void* stream);
+
+/*
+ * ve_gate_v — value-embedding gate (lanjinlin.com.cn repost, "3. Value Embeddings"):
+ *   gate[b,t,h] = 2 * sigmoid(sum_{c<32} x[b,t,c] * Wg[c,h])   (range (0, 2)).
+ * Optionally materialises v_eff = v + gate * ve (pass v, ve, v_eff all non-NULL, or all
+ * NULL). swa_fwd/swa_bwd can instead take (ve, gate) and form v_eff inside their V-tile
+ * loads, which is the fused path.
+ *   x   : device (B,T,ldx) dtype, ldx >= 32 (elements), read.    Wg: device (32,H) float, read.
+ *   gate: device (B,T,H) float, written.
+ */
+int ve_gate_v(const void* x, int ldx, const float* Wg, float* gate, const void* v,
+              const void* ve, void* v_eff, int B, int T, int H, int D, swa_dtype dtype,
+              void* stream);
+
+/*
+ * ve_gate_v_bwd — backward of the gate given dgate = dL/dgate (B,T,H) float (from swa_bwd):
+ *   dz = dgate * gate * (1 - gate/2);  dWg[c,h] = sum_{b,t} x[b,t,c] dz[b,t,h] (overwritten);
+ *   dx32[b,t,c] = sum_h dz[b,t,h] Wg[c,h]   (optional; dx32 NULL skips it).
+ * dWg is reduced in a fixed order (bitwise repeatable).
+ *   dx32: device (B,T,32) dtype, written.
+ */
+int ve_gate_v_bwd(const void* x, int ldx, const float* Wg, const float* gate,
+                  const float* dgate, float* dWg, void* dx32, int B, int T, int H,
+                  swa_dtype dtype, void* stream);
+
+/*
+ * swa_fwd — causal sliding-window attention forward ("GPT-2 124M 复现" §3, §19).
+ *   s_ij = scale * q_i . k_j for max(0, i-W+1) <= j <= i; lse_i = log sum_j exp(s_ij);
+ *   O_i = sum_j exp(s_ij - lse_i) v_eff_j, v_eff = v (+ gate * ve when ve and gate are given).
+ *   q, k, v: device (B,T,H,D) dtype (normally qn, kn from rope_qknorm_fwd), read.
+ *   ve, gate: both NULL, or ve (B,T,H*D) dtype and gate (B,T,H) float, read.
+ *   o  : device (B,T,H,D) dtype, written.     lse: device (B,H,T) float, natural log, written.
+ *   scale: finite, > 0 (1/sqrt(D) for this model).
+ */
+int swa_fwd(const void* q, const void* k, const void* v, const void* ve, const float* gate,
+            void* o, float* lse, int B, int T, int H, int D, int window, float scale,
+            swa_dtype dtype, void* stream);
+
+/* Bytes of workspace swa_bwd needs: the row terms delta (B,H,T) and, for bf16, a float32
+ * dq accumulator (B,T,H,D), each 256-byte aligned inside the block. */
+size_t swa_bwd_workspace_size(int B, int T, int H, int D, swa_dtype dtype);
+
+/*
+ * swa_bwd — backward of swa_fwd with score recomputation ("GPT-2 124M 复现" §19).
+ *   P = exp(s - lse); dv_eff = P^T dO; dP = dO v_eff^T; delta_i = dO_i . O_i;
+ *   dS = P * (dP - delta); dq = scale dS k; dk = scale dS^T q.
+ *   With the gate: dv = dv_eff, dve = gate * dv_eff, dgate = sum_d dv_eff * ve.
+ *   q, k, v, ve, gate: as given to swa_fwd.  o, lse: swa_fwd's outputs.  dO: (B,T,H,D) dtype.
+ *   dq, dk, dv: device (B,T,H,D) dtype, written.
+ *   dve (B,T,H*D) dtype and dgate (B,T,H) float: written when the gate is used (both
+ *   required then), must be NULL otherwise.
+ *   workspace: device, >= swa_bwd_workspace_size() bytes, 256-byte aligned, clobbered.
+ */
+int swa_bwd(const void* q, const void* k, const void* v, const void* ve, const float* gate,
+            const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
+            void* dve, float* dgate, void* workspace, size_t ws_bytes, int B, int T, int H,
+            int D, int window, float scale, swa_dtype dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWA_H_ */

@@ -1,0 +1,145 @@
+"""Shared helpers for the GPU parity tests: device transfer, error metrics, bars, runners."""
+
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from causal_sliding_window_rope_amd import binding as sw
+
+# Parity bars: fp32 path max abs error; bf16 path relative L2 error on O, dQ, dK, dV and max
+# abs error on the logsumexp.
+F32_MAX_ABS = 1e-5
+BF16_REL_L2 = 1e-2
+BF16_LSE_ABS = 2e-3
+
+
+def tdtype(dtype: str):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def dev(a: np.ndarray, dtype: str) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(tdtype(dtype)).cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def rel_l2(a: np.ndarray, b: np.ndarray) -> float:
+    nb = float(np.linalg.norm(b))
+    return float(np.linalg.norm(a - b)) / (nb if nb > 0 else 1.0)
+
+
+def max_abs(a: np.ndarray, b: np.ndarray) -> float:
+    return float(np.max(np.abs(a - b))) if a.size else 0.0
+
+
+def check(name: str, got: np.ndarray, want: np.ndarray, dtype: str, lse: bool = False,
+          sum_scaled: bool = False):
+    """Assert the parity bar of `dtype` for one output.
+
+    sum_scaled: the output is a long fp32 sum whose magnitude grows with its length (dgate is a
+    sum over D); its fp32 bar is 1e-5 relative to max(1, max |want|).
+    """
+    assert got.shape == want.shape, (name, got.shape, want.shape)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    if dtype == "f32":
+        err = max_abs(got, want)
+        if sum_scaled:
+            err /= max(1.0, float(np.max(np.abs(want))))
+        assert err <= F32_MAX_ABS, f"{name}: max abs {err:.3g} > {F32_MAX_ABS}"
+    elif lse:
+        err = max_abs(got, want)
+        assert err <= BF16_LSE_ABS, f"{name}: lse max abs {err:.3g} > {BF16_LSE_ABS}"
+    else:
+        err = rel_l2(got, want)
+        assert err <= BF16_REL_L2, f"{name}: rel L2 {err:.3g} > {BF16_REL_L2}"
+    return err
+
+
+def announce(*parts):
+    print("[case]", *parts, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_layer(x: dict, wl, window: int):
+    """Whole layer on the GPU: prologue, optional gate, swa_fwd, swa_bwd, prologue backward."""
+    dt = wl.dtype
+    q, k, v, dO = (dev(x[n], dt) for n in ("q", "k", "v", "dO"))
+    cs = sw.rope_table(wl.T, wl.D, wl.base)
+    qn, kn = sw.rope_qknorm_fwd(q, k, cs, wl.eps)
+    out = {"qn": qn, "kn": kn}
+    ve = gate = None
+    if wl.gate:
+        xg = dev(x["x"], dt)
+        Wg = torch.from_numpy(x["Wg"]).cuda()
+        ve = dev(x["ve"], dt)
+        gate = sw.ve_gate_v(xg, Wg)
+        out["gate"] = gate
+    o, lse = sw.swa_fwd(qn, kn, v, window, wl.scale, ve=ve, gate=gate)
+    grads = sw.swa_bwd(qn, kn, v, o, lse, dO, window, wl.scale, ve=ve, gate=gate)
+    dqn, dkn, dv = grads[:3]
+    dq, dk = sw.rope_qknorm_bwd(q, k, cs, dqn, dkn, wl.eps)
+    out.update(O=o, lse=lse, dqh=dqn, dkh=dkn, dv=dv, dq=dq, dk=dk)
+    if wl.gate:
+        out["dve"], out["dgate"] = grads[3], grads[4]
+        dWg, dx32 = sw.ve_gate_v_bwd(xg, Wg, gate, grads[4])
+        out["dWg"], out["dx32"] = dWg, dx32
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_layer(x: dict, wl, window: int, sel=None):
+    """Oracle for the same layer; sel = (b, h) restricts to one sequence and head."""
+    f = {n: x[n].astype(np.float64) for n in ("q", "k", "v", "dO")}
+    kw = dict(base=wl.base, eps=wl.eps, scale=wl.scale)
+    gk = {}
+    if wl.gate:
+        B, T = wl.B, wl.T
+        gk = dict(x32=x["x"][..., :32].astype(np.float64), Wg=x["Wg"].astype(np.float64),
+                  ve=x["ve"].astype(np.float64))
+    if sel is not None:
+        b, h = sel
+        f = {n: a[b:b + 1, :, h:h + 1] for n, a in f.items()}
+        if wl.gate:
+            D = wl.D
+            gk = dict(x32=gk["x32"][b:b + 1], Wg=gk["Wg"][:, h:h + 1],
+                      ve=gk["ve"][b:b + 1, :, h * D:(h + 1) * D])
+    fwd = oracle.layer_fwd(f["q"], f["k"], f["v"], window, round_boundary=(wl.dtype == "bf16"),
+                           **kw, **gk)
+    bwd = oracle.layer_bwd(f["q"], f["k"], f["v"], f["dO"], window, fwd, **kw, **gk)
+    return fwd, bwd
+
+
+def compare_layer(g: dict, fwd: dict, bwd: dict, dtype: str, sel=None, gate=False):
+    """Compare GPU outputs (optionally the (b, h) slice) with the oracle; returns errors."""
+    def pick(name, t, layout="bthd"):
+        a = host(t)
+        if sel is None:
+            return a
+        b, h = sel
+        if layout == "bthd":
+            return a[b:b + 1, :, h:h + 1]
+        if layout == "bht":
+            return a[b:b + 1, h:h + 1]
+        if layout == "bth":
+            return a[b:b + 1, :, h:h + 1]
+        raise ValueError(layout)
+
+    errs = {}
+    errs["O"] = check("O", pick("O", g["O"]), fwd["O"], dtype)
+    errs["lse"] = check("lse", pick("lse", g["lse"], "bht"), fwd["lse"], dtype, lse=True)
+    for n in ("dqh", "dkh", "dq", "dk", "dv"):
+        errs[n] = check(n, pick(n, g[n]), bwd[n], dtype)
+    if gate:
+        errs["gate"] = check("gate", pick("gate", g["gate"], "bth"), fwd["g"], "f32")
+        if sel is None:
+            B, T, H, D = g["O"].shape
+            errs["dve"] = check("dve", host(g["dve"]), bwd["dve"], dtype)
+            errs["dgate"] = check("dgate", host(g["dgate"]), bwd["dg"], dtype, sum_scaled=True)
+    return errs

@@ -1,0 +1,114 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function include/swa.h
+declares, and rejects bad arguments on the host before any launch (only fake, never
+dereferenced pointers are passed, and each call fails validation)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from causal_sliding_window_rope_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swa.h")
+
+OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE = 0, 1, 2, 3, 4
+P = ctypes.c_void_p(0x10000)      # aligned fake device pointer (never dereferenced)
+MIS = ctypes.c_void_p(0x10008)    # misaligned fake pointer
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \t\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from causal_sliding_window_rope_amd.build import build
+        build()
+    return binding.load()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("swa_fwd", "swa_bwd", "rope_qknorm_fwd", "rope_qknorm_bwd", "ve_gate_v",
+              "ve_gate_v_bwd", "rope_table", "swa_bwd_workspace_size", "swa_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(lib, n)
+    assert set(binding.SIGNATURES) == set(declared_functions())
+
+
+def _fwd(lib, q=P, k=P, v=P, ve=None, gate=None, o=P, lse=P, B=1, T=8, H=1, D=64, W=4, scale=0.125,
+         dt=1):
+    return lib.swa_fwd(q, k, v, ve, gate, o, lse, B, T, H, D, W, scale, dt, None)
+
+
+def test_swa_fwd_validation(lib):
+    assert _fwd(lib, q=None) == INVALID and b"q must not be NULL" in lib.swa_last_error()
+    assert _fwd(lib, D=96) == UNSUPPORTED
+    assert _fwd(lib, D=32) == UNSUPPORTED
+    assert _fwd(lib, k=MIS) == ALIGN
+    assert _fwd(lib, W=0) == INVALID
+    assert _fwd(lib, W=-2) == INVALID
+    assert _fwd(lib, scale=0.0) == INVALID
+    assert _fwd(lib, scale=float("nan")) == INVALID
+    assert _fwd(lib, B=0) == INVALID
+    assert _fwd(lib, T=0) == INVALID
+    assert _fwd(lib, dt=7) == INVALID
+    assert _fwd(lib, ve=P) == INVALID          # ve without gate
+    assert _fwd(lib, gate=P) == INVALID        # gate without ve
+    assert _fwd(lib, B=1 << 20, T=1 << 12, H=1 << 4, D=128) == UNSUPPORTED
+
+
+def test_swa_bwd_validation(lib):
+    ws_need = lib.swa_bwd_workspace_size(2, 64, 3, 64, 1)
+    assert ws_need >= 2 * 64 * 3 * 4 + 2 * 64 * 3 * 64 * 4
+    assert lib.swa_bwd_workspace_size(2, 64, 3, 96, 1) == 0
+
+    def bwd(ws=P, ws_bytes=ws_need, ve=None, gate=None, dve=None, dgate=None, W=8, dO=P):
+        return lib.swa_bwd(P, P, P, ve, gate, P, P, dO, P, P, P, dve, dgate, ws, ws_bytes, 2, 64, 3,
+                           64, W, 0.125, 1, None)
+
+    assert bwd(ws=None) == WORKSPACE
+    assert bwd(ws_bytes=ws_need - 1) == WORKSPACE
+    assert bwd(ws=ctypes.c_void_p(0x10010)) == ALIGN
+    assert bwd(ve=P, gate=P) == INVALID                 # gate without dve/dgate
+    assert bwd(dve=P, dgate=P) == INVALID               # dve/dgate without gate
+    assert bwd(W=0) == INVALID
+    assert bwd(dO=None) == INVALID
+
+
+def test_prologue_and_gate_validation(lib):
+    assert lib.rope_table(None, 8, 64, 1e4, None) == INVALID
+    assert lib.rope_table(P, 8, 48, 1e4, None) == UNSUPPORTED
+    assert lib.rope_table(P, 8, 64, -1.0, None) == INVALID
+    assert lib.rope_qknorm_fwd(P, P, P, P, P, 1, 8, 1, 64, -1.0, 1, None) == INVALID   # eps < 0
+    assert lib.rope_qknorm_fwd(P, P, P, P, ctypes.c_void_p(0x20000), 1, 8, 1, 64, 1e-6, 1, None) \
+        == INVALID   # qn aliases q
+    assert lib.rope_qknorm_fwd(P, MIS, P, ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000), 1, 8,
+                               1, 64, 1e-6, 1, None) == ALIGN
+    assert lib.rope_qknorm_bwd(P, P, P, None, P, P, P, 1, 8, 1, 64, 1e-6, 1, None) == INVALID
+    assert lib.ve_gate_v(P, 16, P, P, None, None, None, 1, 8, 2, 64, 1, None) == INVALID  # ldx < 32
+    assert lib.ve_gate_v(P, 64, P, P, P, None, None, 1, 8, 2, 64, 1, None) == INVALID    # partial
+    assert lib.ve_gate_v_bwd(P, 64, P, P, None, P, None, 1, 8, 2, 1, None) == INVALID
+    assert lib.swa_last_error()  # message is set
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    x = torch.zeros(1, 8, 1, 64)
+    with pytest.raises(ValueError):
+        binding.swa_fwd(x, x, x, window=4)
