@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Throughput of the attention core (forward + backward) on one MI355X.
+
+One step = the attention of every layer of the nanochat d24 model, forward then backward,
+as in a training step: for layers 0..23 rope_qknorm_fwd + swa_fwd, then for layers 23..0
+swa_bwd (preprocess, main, dq finalize) + rope_qknorm_bwd. Windows follow the 3-short:1-long
+tiling (layers 3, 7, ... full 2048, the rest 1024); B=16 sequences of T=2048, H=12, D=128,
+bf16 storage, fp32 accumulation. Inputs are synthetic N(0, 1) tensors drawn on the device
+from a seeded generator, one set per layer (kernel time does not depend on the values).
+
+The metric counts algorithmic MFMA FLOPs only over visible (query, key) pairs: 4*D per pair
+forward, 10*D per pair backward (the five contractions of the recomputing backward).
+
+Prints one JSON line. --gpus above 1 is refused: this build runs on one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd+bwd TFLOP/s (unmasked FLOPs) and % of MI355X bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+PEAK_HBM_GBS = 8000.0
+
+
+def pairs(T: int, W: int) -> int:
+    W = min(W, T)
+    return W * (W + 1) // 2 + (T - W) * W
+
+
+def layer_list(name: str):
+    from causal_sliding_window_rope_amd.inputs import WORKLOADS, sssl_windows
+    if name == "sssl24":
+        return dict(B=16, T=2048, H=12, D=128, gate=False,
+                    windows=sssl_windows(24, 1024, 2048),
+                    desc="d24 attention sweep: 24 layers, 3-short:1-long windows "
+                         "(18 x 1024, 6 x 2048), B=16, T=2048, H=12, D=128")
+    wl = WORKLOADS[name]
+    return dict(B=wl.B, T=wl.T, H=wl.H, D=wl.D, gate=wl.gate, windows=[wl.window],
+                desc=f"{name}: B={wl.B}, T={wl.T}, H={wl.H}, D={wl.D}, window {wl.window}"
+                     + (", value-embedding gate" if wl.gate else ""))
+
+
+def make_layers(cfg, torch, seed0=1000):
+    """Per-layer device tensors (inputs + forward outputs kept for the backward)."""
+    B, T, H, D = cfg["B"], cfg["T"], cfg["H"], cfg["D"]
+    layers = []
+    for l, W in enumerate(cfg["windows"]):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed0 + l)
+        t = {n: torch.randn((B, T, H, D), generator=g, device="cuda", dtype=torch.float32)
+             .to(torch.bfloat16) for n in ("q", "k", "v", "dO")}
+        t["qn"], t["kn"] = torch.empty_like(t["q"]), torch.empty_like(t["k"])
+        t["o"] = torch.empty_like(t["q"])
+        t["lse"] = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+        if cfg["gate"]:
+            t["x"] = torch.randn((B, T, 1536), generator=g, device="cuda").to(torch.bfloat16)
+            t["Wg"] = torch.randn((32, H), generator=g, device="cuda") * 0.02
+            table = torch.randn((50304, H * D), generator=g, device="cuda").to(torch.bfloat16)
+            ids = torch.randint(0, 50304, (B, T), generator=g, device="cuda")
+            t["ve"] = table[ids].contiguous()
+            del table
+            t["gate"] = torch.empty((B, T, H), dtype=torch.float32, device="cuda")
+        t["W"] = W
+        layers.append(t)
+    return layers
+
+
+def run_bench(args):
+    import torch
+    from causal_sliding_window_rope_amd import binding as sw
+
+    sw.load()  # raises if the HIP library is missing: there is no other path
+    cfg = layer_list(args.workload)
+    B, T, H, D = cfg["B"], cfg["T"], cfg["H"], cfg["D"]
+    scale = D ** -0.5
+    layers = make_layers(cfg, torch)
+    cs = sw.rope_table(T, D, 10000.0)
+    # gradient buffers shared by all layers
+    g = {n: torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
+         for n in ("dqn", "dkn", "dv", "dq", "dk")}
+    if cfg["gate"]:
+        g["dve"] = torch.empty((B, T, H * D), dtype=torch.bfloat16, device="cuda")
+        g["dgate"] = torch.empty((B, T, H), dtype=torch.float32, device="cuda")
+        g["dWg"] = torch.empty((32, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(sw.swa_bwd_workspace_size(B, T, H, D, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+    lib = sw.load()
+    stream = sw._stream()
+    P = sw._ptr
+    nws = ws.numel()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def call(name, *a):
+        st = getattr(lib, name)(*a)
+        if st != 0:
+            raise sw.SwaError(name, st, lib.swa_last_error().decode())
+
+    def step(rec):
+        # forward, layers in order
+        for li, t in enumerate(layers):
+            call("rope_qknorm_fwd", P(t["q"]), P(t["k"]), P(cs), P(t["qn"]), P(t["kn"]), B, T, H, D,
+                 1e-6, sw.SWA_BF16, stream)
+            ve = gate = None
+            if cfg["gate"]:
+                call("ve_gate_v", P(t["x"]), 1536, P(t["Wg"]), P(t["gate"]), None, None, None, B, T,
+                     H, D, sw.SWA_BF16, stream)
+                ve, gate = t["ve"], t["gate"]
+            if rec: rec["fwd"][li][0].record()
+            call("swa_fwd", P(t["qn"]), P(t["kn"]), P(t["v"]), P(ve), P(gate), P(t["o"]), P(t["lse"]),
+                 B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
+            if rec: rec["fwd"][li][1].record()
+        # backward, layers in reverse
+        for li in reversed(range(len(layers))):
+            t = layers[li]
+            ve = gate = dve = dgate = None
+            if cfg["gate"]:
+                ve, gate, dve, dgate = t["ve"], t["gate"], g["dve"], g["dgate"]
+            if rec: rec["bwd"][li][0].record()
+            call("swa_bwd_preprocess", P(t["o"]), P(t["dO"]), P(ws), nws, B, T, H, D, sw.SWA_BF16,
+                 stream)
+            if rec: rec["bwd"][li][1].record()
+            call("swa_bwd_main", P(t["qn"]), P(t["kn"]), P(t["v"]), P(ve), P(gate), P(t["lse"]),
+                 P(t["dO"]), P(g["dqn"]), P(g["dkn"]), P(g["dv"]), P(dve), P(dgate), P(ws), nws,
+                 B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
+            if rec: rec["bwd"][li][2].record()
+            call("swa_bwd_finalize", P(g["dqn"]), P(ws), nws, B, T, H, D, sw.SWA_BF16, stream)
+            if rec: rec["bwd"][li][3].record()
+            call("rope_qknorm_bwd", P(t["q"]), P(t["k"]), P(cs), P(g["dqn"]), P(g["dkn"]), P(g["dq"]),
+                 P(g["dk"]), B, T, H, D, 1e-6, sw.SWA_BF16, stream)
+            if cfg["gate"]:
+                call("ve_gate_v_bwd", P(t["x"]), 1536, P(t["Wg"]), P(gate), P(dgate), P(g["dWg"]),
+                     None, B, T, H, sw.SWA_BF16, stream)
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    nl = len(layers)
+    recs = [{"fwd": [[ev(), ev()] for _ in range(nl)], "bwd": [[ev() for _ in range(4)] for _ in range(nl)]}
+            for _ in range(args.steps)]
+    e0, e1 = ev(), ev()
+    torch.cuda.synchronize()          # one GPU: no process group, so no barrier is needed
+    t0 = time.perf_counter()
+    e0.record()
+    for k in range(args.steps):
+        step(recs[k])
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = e0.elapsed_time(e1) / args.steps
+
+    fwd_ms = sum(r["fwd"][l][0].elapsed_time(r["fwd"][l][1]) for r in recs for l in range(nl))
+    pre_ms = sum(r["bwd"][l][0].elapsed_time(r["bwd"][l][1]) for r in recs for l in range(nl))
+    main_ms = sum(r["bwd"][l][1].elapsed_time(r["bwd"][l][2]) for r in recs for l in range(nl))
+    fin_ms = sum(r["bwd"][l][2].elapsed_time(r["bwd"][l][3]) for r in recs for l in range(nl))
+    launches = args.steps * nl
+
+    npairs = sum(pairs(T, W) for W in cfg["windows"]) * B * H
+    fwd_flop = 4 * D * npairs
+    bwd_flop = 10 * D * npairs
+    flop = fwd_flop + bwd_flop
+    value = flop / (step_ms * 1e-3) / 1e12
+    core_ms = (fwd_ms + pre_ms + main_ms + fin_ms) / args.steps
+    fwd_tf = fwd_flop / (fwd_ms / args.steps * 1e-3) / 1e12
+    bwd_main_tf = bwd_flop / (main_ms / args.steps * 1e-3) / 1e12
+
+    # dominant kernel: the one with the larger share of the step
+    if main_ms >= fwd_ms:
+        dom, dom_ms, dom_flop = "bwd_bf16_kernel (swa_bwd_main)", main_ms / launches, bwd_flop / nl
+    else:
+        dom, dom_ms, dom_flop = "fwd_bf16_kernel (swa_fwd)", fwd_ms / launches, fwd_flop / nl
+    achieved = dom_flop / (dom_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "avg_launch_us": round(dom_ms * 1e3, 2),
+                "traffic": traffic_from_profile(dom, args.workload)}
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg["desc"], "global_batch": B, "seq_len": T, "heads": H,
+                   "head_dim": D, "windows": sorted(set(cfg["windows"])),
+                   "parallelism": "single GPU"},
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "breakdown": {
+            "algorithmic_tflop_per_step": round(flop / 1e12, 4),
+            "attention_core_ms_per_step": round(core_ms, 4),
+            "attention_core_tflops": round(flop / (core_ms * 1e-3) / 1e12, 2),
+            "attention_core_pct_of_peak": round(100 * flop / (core_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "prologue_and_gate_ms_per_step": round(step_ms - core_ms, 4),
+            "swa_fwd_tflops": round(fwd_tf, 2),
+            "swa_bwd_main_tflops": round(bwd_main_tf, 2),
+            "swa_fwd_ms_per_step": round(fwd_ms / args.steps, 4),
+            "swa_bwd_preprocess_ms_per_step": round(pre_ms / args.steps, 4),
+            "swa_bwd_main_ms_per_step": round(main_ms / args.steps, 4),
+            "swa_bwd_finalize_ms_per_step": round(fin_ms / args.steps, 4),
+            "wall_s_timed_region": round(wall, 3),
+        },
+        "roofline": roofline,
+    }
+    return result
+
+
+def traffic_from_profile(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
+    current kernel source (its sha256 is recorded there); otherwise None."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            prof = json.load(f)
+    except (OSError, ValueError):
+        return None
+    key = "bwd" if kernel.startswith("bwd") else "fwd"
+    ent = prof.get(workload, {}).get(key)
+    if not ent:
+        return None
+    src = os.path.join(ROOT, "causal_sliding_window_rope_amd", "csrc", ent["source"])
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != ent["source_sha256"]:
+            return None
+    return ent["hbm_bytes_per_launch"]
+
+
+def cpu_baseline(args):
+    """The fp64 numpy oracle, as it stands, on a bounded sample of the same workload: whole
+    (b, h) heads of a short (1024) and a full (2048) d24 layer, prologue + attention forward and
+    backward + prologue backward, until about args.cpu_seconds of CPU work."""
+    import numpy as np
+    import oracle
+    from causal_sliding_window_rope_amd.inputs import make_inputs, small_workload
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    cfg = layer_list(args.workload)
+    T, D = cfg["T"], cfg["D"]
+    wins = sorted(set(cfg["windows"]))
+    done_flop, secs, heads = 0, 0.0, {}
+    hcount = 0
+    while secs < args.cpu_seconds and hcount < 512:
+        W = wins[hcount % len(wins)]
+        wl = small_workload(1, T, 1, D, W, "bf16", seed=9000 + hcount)
+        x = make_inputs(wl)
+        f = {n: x[n].astype(np.float64) for n in ("q", "k", "v", "dO")}
+        t0 = time.perf_counter()
+        fwd = oracle.layer_fwd(f["q"], f["k"], f["v"], W, round_boundary=True)
+        oracle.layer_bwd(f["q"], f["k"], f["v"], f["dO"], W, fwd)
+        secs += time.perf_counter() - t0
+        done_flop += 14 * D * pairs(T, W)
+        heads[W] = heads.get(W, 0) + 1
+        hcount += 1
+    sample = ", ".join(f"{n} head(s) of T={T}, D={D}, window {w}" for w, n in sorted(heads.items()))
+    return {"value": round(done_flop / secs / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle, prologue + fwd + bwd of {sample}; "
+                      f"{secs:.1f} s; {len(os.sched_getaffinity(0))} cores visible, "
+                      f"{platform.processor() or platform.machine()}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="sssl24",
+                    choices=["sssl24", "d24_short", "d24_full", "gpt2_124m", "d24_short_ve"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported; this build measures one GPU "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    res = run_bench(args)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

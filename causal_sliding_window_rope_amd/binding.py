@@ -36,6 +36,10 @@ SIGNATURES = {
     "swa_bwd_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "swa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
                      _I, _I, _I, _I, _I, _F, _I, _P]),
+    "swa_bwd_preprocess": (_I, [_P, _P, _P, _S, _I, _I, _I, _I, _I, _P]),
+    "swa_bwd_main": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
+                          _I, _I, _I, _I, _I, _F, _I, _P]),
+    "swa_bwd_finalize": (_I, [_P, _P, _S, _I, _I, _I, _I, _I, _P]),
 }
 
 _lib = None
@@ -197,6 +201,37 @@ def swa_bwd(q, k, v, o, lse, dO, window: int, scale: float | None = None, ve=Non
           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dve), _ptr(dgate), _ptr(workspace),
           workspace.numel() * workspace.element_size(), B, T, H, D, int(window), float(scale),
           _dt(q), _stream())
+    if ve is not None:
+        return dq, dk, dv, dve, dgate
+    return dq, dk, dv
+
+
+def swa_bwd_stages(q, k, v, o, lse, dO, window: int, scale: float | None = None, ve=None,
+                   gate=None, workspace=None, grads=None, events=None):
+    """swa_bwd as its three C-ABI stages. ``events`` = (start, end) torch.cuda.Event pair
+    recorded around swa_bwd_main on the current stream (for timing the main kernel)."""
+    B, T, H, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    ws_bytes = swa_bwd_workspace_size(B, T, H, D, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    if grads is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dve = torch.empty_like(ve) if ve is not None else None
+        dgate = torch.empty((B, T, H), dtype=torch.float32, device=q.device) if ve is not None else None
+    else:
+        dq, dk, dv, dve, dgate = grads
+    st = _stream()
+    _call("swa_bwd_preprocess", _ptr(o), _ptr(dO), _ptr(workspace), nbytes, B, T, H, D, _dt(q), st)
+    if events is not None:
+        events[0].record()
+    _call("swa_bwd_main", _ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), _ptr(lse), _ptr(dO),
+          _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dve), _ptr(dgate), _ptr(workspace), nbytes, B, T, H, D,
+          int(window), float(scale), _dt(q), st)
+    if events is not None:
+        events[1].record()
+    _call("swa_bwd_finalize", _ptr(dq), _ptr(workspace), nbytes, B, T, H, D, _dt(q), st)
     if ve is not None:
         return dq, dk, dv, dve, dgate
     return dq, dk, dv

@@ -72,6 +72,17 @@ int check_window_scale(const char* fn, int window, float scale, int T, int* w_ou
   return 0;
 }
 
+int check_ws(const char* fn, const void* workspace, size_t ws_bytes, int B, int T, int H, int D,
+             int dtype) {
+  const size_t need_ws = swa::bwd_workspace_bytes(B, T, H, D, dtype == SWA_BF16);
+  if (!workspace || ws_bytes < need_ws)
+    return fail(SWA_ERR_WORKSPACE, "%s: workspace of %zu bytes required (got %zu)", fn, need_ws,
+                workspace ? ws_bytes : (size_t)0);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(SWA_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+  return 0;
+}
+
 }  // namespace
 
 #define SWA_TRY(expr)        \
@@ -170,14 +181,15 @@ size_t swa_bwd_workspace_size(int B, int T, int H, int D, swa_dtype dtype) {
   return swa::bwd_workspace_bytes(B, T, H, D, dtype == SWA_BF16);
 }
 
-int swa_bwd(const void* q, const void* k, const void* v, const void* ve, const float* gate,
-            const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
-            void* dve, float* dgate, void* workspace, size_t ws_bytes, int B, int T, int H, int D,
-            int window, float scale, swa_dtype dtype, void* stream) {
-  const char* fn = "swa_bwd";
+static int check_bwd(const char* fn, const void* q, const void* k, const void* v, const void* ve,
+                     const float* gate, const void* o, const float* lse, const void* dO,
+                     const void* dq, const void* dk, const void* dv, const void* dve,
+                     const float* dgate, const void* workspace, size_t ws_bytes, int B, int T,
+                     int H, int D, int window, float scale, swa_dtype dtype, swa::AttnShape* a) {
   SWA_TRY(check_shape(fn, B, T, H, D, dtype));
   SWA_TRY(need(fn, "q", q)); SWA_TRY(need(fn, "k", k)); SWA_TRY(need(fn, "v", v));
-  SWA_TRY(need(fn, "o", o)); SWA_TRY(need(fn, "lse", lse)); SWA_TRY(need(fn, "dO", dO));
+  if (o) SWA_TRY(need(fn, "o", o));
+  SWA_TRY(need(fn, "lse", lse)); SWA_TRY(need(fn, "dO", dO));
   SWA_TRY(need(fn, "dq", dq)); SWA_TRY(need(fn, "dk", dk)); SWA_TRY(need(fn, "dv", dv));
   const bool g = gate != nullptr;
   if ((ve != nullptr) != g)
@@ -185,16 +197,59 @@ int swa_bwd(const void* q, const void* k, const void* v, const void* ve, const f
   if (g != (dve != nullptr) || g != (dgate != nullptr))
     return fail(SWA_ERR_INVALID_ARG, "%s: dve and dgate are required with the gate, NULL without", fn);
   SWA_TRY(opt(fn, "ve", ve)); SWA_TRY(opt(fn, "dve", dve));
-  swa::AttnShape a{B, T, H, D, 0, scale};
-  SWA_TRY(check_window_scale(fn, window, scale, T, &a.window));
-  const size_t need_ws = swa::bwd_workspace_bytes(B, T, H, D, dtype == SWA_BF16);
-  if (!workspace || ws_bytes < need_ws)
-    return fail(SWA_ERR_WORKSPACE, "%s: workspace of %zu bytes required (got %zu)", fn, need_ws,
-                workspace ? ws_bytes : (size_t)0);
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(SWA_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
-  return hip_status(swa::launch_bwd(a, q, k, v, ve, gate, o, lse, dO, dq, dk, dv, dve, dgate,
-                                    workspace, dtype == SWA_BF16, (hipStream_t)stream), fn);
+  *a = swa::AttnShape{B, T, H, D, 0, scale};
+  SWA_TRY(check_window_scale(fn, window, scale, T, &a->window));
+  return check_ws(fn, workspace, ws_bytes, B, T, H, D, dtype);
+}
+
+int swa_bwd(const void* q, const void* k, const void* v, const void* ve, const float* gate,
+            const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
+            void* dve, float* dgate, void* workspace, size_t ws_bytes, int B, int T, int H, int D,
+            int window, float scale, swa_dtype dtype, void* stream) {
+  const char* fn = "swa_bwd";
+  swa::AttnShape a;
+  SWA_TRY(need(fn, "o", o));
+  SWA_TRY(check_bwd(fn, q, k, v, ve, gate, o, lse, dO, dq, dk, dv, dve, dgate, workspace,
+                    ws_bytes, B, T, H, D, window, scale, dtype, &a));
+  const bool bf = dtype == SWA_BF16;
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e = swa::launch_bwd_pre(a, o, dO, workspace, bf, s);
+  if (e == hipSuccess)
+    e = swa::launch_bwd_main(a, q, k, v, ve, gate, lse, dO, dq, dk, dv, dve, dgate, workspace, bf, s);
+  if (e == hipSuccess) e = swa::launch_bwd_final(a, dq, workspace, bf, s);
+  return hip_status(e, fn);
+}
+
+int swa_bwd_preprocess(const void* o, const void* dO, void* workspace, size_t ws_bytes, int B,
+                       int T, int H, int D, swa_dtype dtype, void* stream) {
+  const char* fn = "swa_bwd_preprocess";
+  SWA_TRY(check_shape(fn, B, T, H, D, dtype));
+  SWA_TRY(need(fn, "o", o)); SWA_TRY(need(fn, "dO", dO));
+  SWA_TRY(check_ws(fn, workspace, ws_bytes, B, T, H, D, dtype));
+  swa::AttnShape a{B, T, H, D, T, 1.f};
+  return hip_status(swa::launch_bwd_pre(a, o, dO, workspace, dtype == SWA_BF16, (hipStream_t)stream), fn);
+}
+
+int swa_bwd_main(const void* q, const void* k, const void* v, const void* ve, const float* gate,
+                 const float* lse, const void* dO, void* dq, void* dk, void* dv, void* dve,
+                 float* dgate, void* workspace, size_t ws_bytes, int B, int T, int H, int D,
+                 int window, float scale, swa_dtype dtype, void* stream) {
+  const char* fn = "swa_bwd_main";
+  swa::AttnShape a;
+  SWA_TRY(check_bwd(fn, q, k, v, ve, gate, nullptr, lse, dO, dq, dk, dv, dve, dgate, workspace,
+                    ws_bytes, B, T, H, D, window, scale, dtype, &a));
+  return hip_status(swa::launch_bwd_main(a, q, k, v, ve, gate, lse, dO, dq, dk, dv, dve, dgate,
+                                         workspace, dtype == SWA_BF16, (hipStream_t)stream), fn);
+}
+
+int swa_bwd_finalize(void* dq, void* workspace, size_t ws_bytes, int B, int T, int H, int D,
+                     swa_dtype dtype, void* stream) {
+  const char* fn = "swa_bwd_finalize";
+  SWA_TRY(check_shape(fn, B, T, H, D, dtype));
+  SWA_TRY(need(fn, "dq", dq));
+  SWA_TRY(check_ws(fn, workspace, ws_bytes, B, T, H, D, dtype));
+  swa::AttnShape a{B, T, H, D, T, 1.f};
+  return hip_status(swa::launch_bwd_final(a, dq, workspace, dtype == SWA_BF16, (hipStream_t)stream), fn);
 }
 
 }  // extern "C"

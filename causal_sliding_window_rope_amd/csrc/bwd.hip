@@ -525,54 +525,78 @@ static hipError_t launch_bwd_bf16_t(const AttnShape& a, const bwdk::Params& p, h
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const AttnShape& a, const void* q, const void* k, const void* v,
-                      const void* ve, const float* gate, const void* o, const float* lse,
-                      const void* dO, void* dq, void* dk, void* dv, void* dve, float* dgate,
-                      void* ws, bool is_bf16, hipStream_t s) {
-  const int B = a.B, T = a.T, H = a.H, D = a.D;
-  float* delta = reinterpret_cast<float*>(ws);
-  float* dq_acc = is_bf16 ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
-                                                  align256((size_t)B * H * T * sizeof(float)))
-                       : nullptr;
+namespace {
+struct WsView {
+  float* delta;
+  float* dq_acc;  // bf16 path only
+};
+WsView ws_view(void* ws, int B, int T, int H, bool is_bf16) {
+  WsView w;
+  w.delta = reinterpret_cast<float*>(ws);
+  w.dq_acc = is_bf16 ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
+                                                align256((size_t)B * H * T * sizeof(float)))
+                     : nullptr;
+  return w;
+}
+}  // namespace
+
+hipError_t launch_bwd_pre(const AttnShape& a, const void* o, const void* dO, void* ws,
+                          bool is_bf16, hipStream_t s) {
+  const WsView w = ws_view(ws, a.B, a.T, a.H, is_bf16);
   if (is_bf16) {
-    if (D == 64) launch_pre<swa::bf16, 64>(o, dO, delta, dq_acc, B, T, H, s);
-    else launch_pre<swa::bf16, 128>(o, dO, delta, dq_acc, B, T, H, s);
+    if (a.D == 64) launch_pre<swa::bf16, 64>(o, dO, w.delta, w.dq_acc, a.B, a.T, a.H, s);
+    else launch_pre<swa::bf16, 128>(o, dO, w.delta, w.dq_acc, a.B, a.T, a.H, s);
+  } else {
+    if (a.D == 64) launch_pre<float, 64>(o, dO, w.delta, nullptr, a.B, a.T, a.H, s);
+    else launch_pre<float, 128>(o, dO, w.delta, nullptr, a.B, a.T, a.H, s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_main(const AttnShape& a, const void* q, const void* k, const void* v,
+                           const void* ve, const float* gate, const float* lse, const void* dO,
+                           void* dq, void* dk, void* dv, void* dve, float* dgate, void* ws,
+                           bool is_bf16, hipStream_t s) {
+  const int B = a.B, T = a.T, H = a.H, D = a.D;
+  const WsView w = ws_view(ws, B, T, H, is_bf16);
+  if (is_bf16) {
     bwdk::Params p;
     p.q = (const bf16*)q; p.k = (const bf16*)k; p.v = (const bf16*)v; p.ve = (const bf16*)ve;
-    p.gate = gate; p.lse = lse; p.delta = delta; p.dO = (const bf16*)dO; p.dq_acc = dq_acc;
+    p.gate = gate; p.lse = lse; p.delta = w.delta; p.dO = (const bf16*)dO; p.dq_acc = w.dq_acc;
     p.dk = (bf16*)dk; p.dv = (bf16*)dv; p.dve = (bf16*)dve; p.dgate = dgate;
     p.B = B; p.T = T; p.H = H; p.window = a.window;
     p.nkb = (T + bwdk::BNK - 1) / bwdk::BNK;
     p.c = a.scale * kLog2e;
     p.scale = a.scale;
     const bool g = gate != nullptr;
-    hipError_t e;
-    if (D == 64) e = g ? launch_bwd_bf16_t<64, true>(a, p, s) : launch_bwd_bf16_t<64, false>(a, p, s);
-    else e = g ? launch_bwd_bf16_t<128, true>(a, p, s) : launch_bwd_bf16_t<128, false>(a, p, s);
-    if (e != hipSuccess) return e;
-    const size_t n8 = (size_t)B * T * H * D / 8;
-    hipLaunchKernelGGL(bwd_dq_final_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s,
-                       dq_acc, (bf16*)dq, n8);
-    return hipGetLastError();
+    if (D == 64) return g ? launch_bwd_bf16_t<64, true>(a, p, s) : launch_bwd_bf16_t<64, false>(a, p, s);
+    return g ? launch_bwd_bf16_t<128, true>(a, p, s) : launch_bwd_bf16_t<128, false>(a, p, s);
   }
-  if (D == 64) launch_pre<float, 64>(o, dO, delta, nullptr, B, T, H, s);
-  else launch_pre<float, 128>(o, dO, delta, nullptr, B, T, H, s);
   dim3 grid(T, B * H);
   if (D == 64) {
     hipLaunchKernelGGL(bwd_dkdv_f32_kernel<64>, grid, dim3(64), 0, s, (const float*)q, (const float*)k,
-                       (const float*)v, (const float*)ve, gate, lse, delta, (const float*)dO,
+                       (const float*)v, (const float*)ve, gate, lse, w.delta, (const float*)dO,
                        (float*)dk, (float*)dv, (float*)dve, dgate, T, H, a.window, a.scale);
     hipLaunchKernelGGL(bwd_dq_f32_kernel<64>, grid, dim3(64), 0, s, (const float*)q, (const float*)k,
-                       (const float*)v, (const float*)ve, gate, lse, delta, (const float*)dO,
+                       (const float*)v, (const float*)ve, gate, lse, w.delta, (const float*)dO,
                        (float*)dq, T, H, a.window, a.scale);
   } else {
     hipLaunchKernelGGL(bwd_dkdv_f32_kernel<128>, grid, dim3(64), 0, s, (const float*)q, (const float*)k,
-                       (const float*)v, (const float*)ve, gate, lse, delta, (const float*)dO,
+                       (const float*)v, (const float*)ve, gate, lse, w.delta, (const float*)dO,
                        (float*)dk, (float*)dv, (float*)dve, dgate, T, H, a.window, a.scale);
     hipLaunchKernelGGL(bwd_dq_f32_kernel<128>, grid, dim3(64), 0, s, (const float*)q, (const float*)k,
-                       (const float*)v, (const float*)ve, gate, lse, delta, (const float*)dO,
+                       (const float*)v, (const float*)ve, gate, lse, w.delta, (const float*)dO,
                        (float*)dq, T, H, a.window, a.scale);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_final(const AttnShape& a, void* dq, void* ws, bool is_bf16, hipStream_t s) {
+  if (!is_bf16) return hipSuccess;  // the fp32 path writes dq directly
+  const WsView w = ws_view(ws, a.B, a.T, a.H, is_bf16);
+  const size_t n8 = (size_t)a.B * a.T * a.H * a.D / 8;
+  hipLaunchKernelGGL(bwd_dq_final_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s,
+                     w.dq_acc, (bf16*)dq, n8);
   return hipGetLastError();
 }
 

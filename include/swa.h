@@ -159,6 +159,32 @@ int swa_bwd(const void* q, const void* k, const void* v, const void* ve, const f
             void* dve, float* dgate, void* workspace, size_t ws_bytes, int B, int T, int H,
             int D, int window, float scale, swa_dtype dtype, void* stream);
 
+/*
+ * The three stages swa_bwd runs, for callers that schedule or time them separately. Call them
+ * in this order on one stream with one workspace (same sizes and dtype throughout):
+ *
+ * swa_bwd_preprocess — delta_i = dO_i . O_i into the workspace; for SWA_BF16 also zeroes the
+ *   float32 dq accumulator in the workspace.
+ */
+int swa_bwd_preprocess(const void* o, const void* dO, void* workspace, size_t ws_bytes, int B,
+                       int T, int H, int D, swa_dtype dtype, void* stream);
+
+/*
+ * swa_bwd_main — the recomputing backward proper (arguments as swa_bwd, without o). Writes dk,
+ *   dv (dve, dgate); writes dq for SWA_F32; for SWA_BF16 adds scale * dS k into the workspace's
+ *   dq accumulator (dq itself is written by swa_bwd_finalize).
+ */
+int swa_bwd_main(const void* q, const void* k, const void* v, const void* ve, const float* gate,
+                 const float* lse, const void* dO, void* dq, void* dk, void* dv, void* dve,
+                 float* dgate, void* workspace, size_t ws_bytes, int B, int T, int H, int D,
+                 int window, float scale, swa_dtype dtype, void* stream);
+
+/*
+ * swa_bwd_finalize — SWA_BF16: dq = bf16(dq accumulator). SWA_F32: validates and does nothing.
+ */
+int swa_bwd_finalize(void* dq, void* workspace, size_t ws_bytes, int B, int T, int H, int D,
+                     swa_dtype dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
