@@ -46,6 +46,8 @@ def _compile(src: str, extra: list[str]) -> str:
 
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    if os.path.exists(OUT):
+        os.remove(OUT)   # a failed build must not leave an older library behind
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra or []), srcs))

@@ -46,6 +46,32 @@ __device__ __forceinline__ float half_swap(float v) {
   return (threadIdx.x & 32) ? __uint_as_float(r[0]) : __uint_as_float(r[1]);
 }
 
+// LDS-qualified pointers (address space 3).
+template <typename T> using lds_t = __attribute__((address_space(3))) T;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Asynchronous 16-byte global -> LDS copy: lane l of the wave writes lds_base + 16*l bytes
+// (lds_base must be the same for the whole wave).
+__device__ __forceinline__ void g2lds16(const void* gsrc, lds_t<bf16>* lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_t<void>*)lds_base, 16, 0, 0);
+}
+
+// Wait until this wave's outstanding vector-memory operations (incl. LDS DMA) have completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// Transposing LDS read: each 16-lane group reads a 4 x 16 block of b16 (lane j gives the
+// address of row j/4, columns 4(j%4)..+3) and lane i receives column i, rows 0..3.
+__device__ __forceinline__ bf16x4 ds_read_tr16(const lds_t<bf16>* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_t<s16x4>*)p);
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+// Bank swizzle of 16-byte chunk positions within a tile row (XOR with a function of the row):
+// keeps the 128-bit row reads of 8 consecutive rows and the transposing reads of 4
+// consecutive rows free of bank conflicts.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

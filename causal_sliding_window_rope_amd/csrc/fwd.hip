@@ -33,21 +33,13 @@ constexpr int BM = 32 * NW;    // query rows per workgroup
 constexpr int BN = 64;         // keys per tile
 
 template <int D> struct Cfg {
-  static constexpr int KP = D + 8;          // K tile row pitch (bf16 elements)
-  static constexpr int VP = BN + 8;         // V^T tile row pitch
-  static constexpr int K_ELEMS = BN * KP;
-  static constexpr int V_ELEMS = D * VP;
-  static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
-  static constexpr int KG = (D == 128) ? 4 : 2;      // keys per V staging unit
-  static constexpr int KGROUPS = BN / KG;             // 16 or 32
-  static constexpr int K_CHUNKS = BN * D / 8 / 256;   // 16-byte K chunks per thread
+  static constexpr int CH = D / 8;          // 16-byte chunks per row
+  static constexpr int RPI = 64 / CH;       // rows per wave-wide 1 KiB load
+  static constexpr int NI = BN / RPI;       // 1 KiB loads per tile
+  static constexpr int NIW = NI / NW;       // ... per wave
+  static constexpr int TILE = BN * D;       // elements per K or V tile
+  static constexpr int CPT = BN * CH / 256; // chunks per thread (register-staged gate path)
 };
-
-// Position of key `k` (0..63) of a tile inside a V^T row: bits 2 and 3 swapped, which puts the
-// 8 keys one lane feeds to a PV k-step next to each other.
-__device__ __forceinline__ int vt_pos(int k) {
-  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
-}
 
 struct Params {
   const bf16* q; const bf16* k; const bf16* v; const bf16* ve; const float* gate;
@@ -56,93 +48,161 @@ struct Params {
   float c;      // scale * log2(e)
 };
 
+// Online-softmax reference updates only when a row max grows by more than 2^8 (see kernel).
+constexpr float kRescaleSlack = 8.0f;
+
 template <int D, bool GATE>
-struct Stage {
+struct Tiles {
   using C = Cfg<D>;
-  uint4 kw[C::K_CHUNKS];
-  uint4 vw[C::KG];
-  float g[C::KG];
-  uint4 ew[GATE ? C::KG : 1];
-
-  __device__ __forceinline__ void load(const Params& p, int b, int h, int kt, int tid) {
-    const int T = p.T, H = p.H;
-    // K rows, 16-byte chunks, row-major
+  // Issue the asynchronous loads of key tile kt into (ks, vs). Every lane moves one 16-byte
+  // chunk per 1 KiB wave load; lane l of load I lands at row I*RPI + l/CH, position l%CH, and
+  // fetches source chunk (l%CH) ^ swz(row). Rows past the sequence end re-read row T-1 (their
+  // scores are masked).
+  __device__ __forceinline__ static void load(const Params& p, const bf16* kbase, const bf16* vbase,
+                                              lds_t<bf16>* ks, lds_t<bf16>* vs, int kt, int wave,
+                                              int lane, int tid) {
+    const int T = p.T;
+    const size_t rs = (size_t)p.H * D;   // row stride in elements
 #pragma unroll
-    for (int r = 0; r < C::K_CHUNKS; ++r) {
-      const int c = tid + 256 * r;
-      const int key = c / (D / 8), dc = c % (D / 8);
-      const int kg = kt * BN + key;
-      if (kg < T) kw[r] = *reinterpret_cast<const uint4*>(p.k + (((size_t)b * T + kg) * H + h) * D + dc * 8);
-      else kw[r] = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < C::NIW; ++i) {
+      const int I = wave * C::NIW + i;
+      const int r = I * C::RPI + lane / C::CH;
+      const int c = (lane % C::CH) ^ swz(r);
+      const size_t goff = (size_t)min(kt * BN + r, T - 1) * rs + 8 * c;
+      g2lds16(kbase + goff, ks + I * C::RPI * D);
+      if constexpr (!GATE) g2lds16(vbase + goff, vs + I * C::RPI * D);
     }
-    // V: KG consecutive keys x 8 dims
-    const int kgrp = tid % C::KGROUPS, dgrp = tid / C::KGROUPS;
+    if constexpr (GATE) {
+      // v_eff = v + gate * ve is formed in fp32 on the way into LDS
 #pragma unroll
-    for (int j = 0; j < C::KG; ++j) {
-      const int kg = kt * BN + kgrp * C::KG + j;
-      if (kg < T) {
-        const size_t row = ((size_t)b * T + kg) * H + h;
-        vw[j] = *reinterpret_cast<const uint4*>(p.v + row * D + dgrp * 8);
-        if constexpr (GATE) {
-          ew[j] = *reinterpret_cast<const uint4*>(p.ve + row * D + dgrp * 8);
-          g[j] = p.gate[row];
-        }
-      } else {
-        vw[j] = make_uint4(0, 0, 0, 0);
-        if constexpr (GATE) { ew[j] = make_uint4(0, 0, 0, 0); g[j] = 0.f; }
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(bf16* buf, int tid) {
-    bf16* ks = buf;
-    bf16* vs = buf + C::K_ELEMS;
-#pragma unroll
-    for (int r = 0; r < C::K_CHUNKS; ++r) {
-      const int c = tid + 256 * r;
-      const int key = c / (D / 8), dc = c % (D / 8);
-      *reinterpret_cast<uint4*>(ks + key * C::KP + dc * 8) = kw[r];
-    }
-    const int kgrp = tid % C::KGROUPS, dgrp = tid / C::KGROUPS;
-    // unpack to floats: f[j][e] = V[key j][d = dgrp*8 + e]
-    float f[C::KG][8];
-#pragma unroll
-    for (int j = 0; j < C::KG; ++j) {
-      const uint32_t w[4] = {vw[j].x, vw[j].y, vw[j].z, vw[j].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { f[j][2 * e] = bf_lo(w[e]); f[j][2 * e + 1] = bf_hi(w[e]); }
-      if constexpr (GATE) {
-        const uint32_t u[4] = {ew[j].x, ew[j].y, ew[j].z, ew[j].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          f[j][2 * e] = fmaf(g[j], bf_lo(u[e]), f[j][2 * e]);
-          f[j][2 * e + 1] = fmaf(g[j], bf_hi(u[e]), f[j][2 * e + 1]);
-        }
-      }
-    }
-    const int pos = vt_pos(kgrp * C::KG);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      bf16* dst = vs + (dgrp * 8 + e) * C::VP + pos;
-      if constexpr (C::KG == 4) {
-        uint2 w;
-        w.x = pack_bf2(f[0][e], f[1][e]);
-        w.y = pack_bf2(f[2][e], f[3][e]);
-        *reinterpret_cast<uint2*>(dst) = w;
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = pack_bf2(f[0][e], f[1][e]);
+      for (int j = 0; j < C::CPT; ++j) {
+        const int id = tid + 256 * j;
+        const int r = id / C::CH, pos = id % C::CH;
+        const int c = pos ^ swz(r);
+        const int row = min(kt * BN + r, T - 1);
+        const size_t goff = (size_t)row * rs + 8 * c;
+        const uint4 a = *reinterpret_cast<const uint4*>(vbase + goff);
+        const uint4 e = *reinterpret_cast<const uint4*>(p.ve + (vbase - p.v) + goff);
+        const float g = p.gate[(vbase - p.v) / D + (size_t)row * p.H];
+        uint4 o;
+        o.x = pack_bf2(fmaf(g, bf_lo(e.x), bf_lo(a.x)), fmaf(g, bf_hi(e.x), bf_hi(a.x)));
+        o.y = pack_bf2(fmaf(g, bf_lo(e.y), bf_lo(a.y)), fmaf(g, bf_hi(e.y), bf_hi(a.y)));
+        o.z = pack_bf2(fmaf(g, bf_lo(e.z), bf_lo(a.z)), fmaf(g, bf_hi(e.z), bf_hi(a.z)));
+        o.w = pack_bf2(fmaf(g, bf_lo(e.w), bf_lo(a.w)), fmaf(g, bf_hi(e.w), bf_hi(a.w)));
+        *reinterpret_cast<lds_t<u32x4>*>(vs + r * D + 8 * pos) = (u32x4){o.x, o.y, o.z, o.w};
       }
     }
   }
 };
 
+template <int D>
+struct WaveState {
+  static constexpr int NDB = D / 32;
+  f32x16 oacc[NDB];
+  float m_ref, l_run;
+};
+
+// One 64-key tile for one wave (32 query rows): S^T = K Q^T, mask, online softmax, O^T += V^T P^T.
+template <int D>
+__device__ __forceinline__ void tile_step(WaveState<D>& ws, const bf16x8* qreg,
+                                          const lds_t<bf16>* ks, const lds_t<bf16>* vs, int k0,
+                                          int qw, int myq, int T, int W, float c, int lane) {
+  constexpr int NKS = D / 16, NDB = D / 32;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const bool skip = (k0 > qw + 31) || (k0 + BN - 1 < qw - W + 1);
+  if (skip) return;
+  const bool need_mask = (k0 + BN - 1 > qw) || (k0 < qw + 31 - W + 1) || (k0 + BN > T);
+  f32x16 s[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    s[kb] = (f32x16){};
+    const int m = kb * 32 + l32;
+    const lds_t<bf16>* arow = ks + m * D;
+    const int sw = swz(m);
+#pragma unroll
+    for (int kk = 0; kk < NKS; ++kk) {
+      const bf16x8 a = *reinterpret_cast<const lds_t<bf16x8>*>(arow + 8 * ((2 * kk + hi) ^ sw));
+      s[kb] = mfma32(a, qreg[kk], s[kb]);
+    }
+  }
+  if (need_mask) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kg = k0 + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
+        const bool ok = (kg <= myq) && (kg > myq - W) && (kg < T);
+        s[kb][i] = ok ? s[kb][i] : -INFINITY;
+      }
+  }
+  float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = (kb == 0 ? 2 : 0); i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kb][i], s[kb][i + 1]));
+  mx = fmaxf(mx, half_swap(mx));
+  const float mt = mx * c;
+  // Lazy rescale: the reference m_ref only moves when some row's max exceeds it by more than
+  // kRescaleSlack (in log2 units), so exp2(s*c - m_ref) <= 2^8 and the O rescale is rare.
+  // Every term of a row is weighted against the same reference, so the result is exact.
+  if (__builtin_amdgcn_ballot_w64(mt > ws.m_ref + kRescaleSlack) != 0) {
+    const float m_new = fmaxf(ws.m_ref, mt);
+    const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(ws.m_ref - m_new);
+    ws.l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) ws.oacc[db] *= alpha;
+    ws.m_ref = m_new;
+  }
+  const float m_use = (ws.m_ref == -INFINITY) ? 0.f : ws.m_ref;
+  float lsum = 0.f;
+  bf16x8 pb[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp) {
+      float e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        e[j] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * sp + j], c, -m_use));
+        lsum += e[j];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const bf16x2 t = __builtin_convertvector((f32x2){e[j], e[j + 1]}, bf16x2);
+        pb[kb][sp][j] = t[0];
+        pb[kb][sp][j + 1] = t[1];
+      }
+    }
+  ws.l_run += lsum;
+  // O^T += V^T P^T; the V^T operand comes from the row-major V tile by transposing reads.
+  const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int d = 32 * db + 16 * (g & 1) + 4 * (j & 3);
+    const int cc = d >> 3, half = (d >> 2) & 1;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int sp = 0; sp < 2; ++sp) {
+        const int r1 = kb * 32 + sp * 16 + 4 * hi + (j >> 2), r2 = r1 + 8;
+        const bf16x4 lo = ds_read_tr16(vs + r1 * D + 8 * (cc ^ swz(r1)) + 4 * half);
+        const bf16x4 up = ds_read_tr16(vs + r2 * D + 8 * (cc ^ swz(r2)) + 4 * half);
+        const bf16x8 a = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+        ws.oacc[db] = mfma32(a, pb[kb][sp], ws.oacc[db]);
+      }
+  }
+}
+
 template <int D, bool GATE>
-__global__ void __launch_bounds__(256) fwd_bf16_kernel(Params p) {
+__global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(Params p) {
   using C = Cfg<D>;
-  constexpr int NDB = D / 32;  // 32-wide d blocks of O^T
-  constexpr int NKS = D / 16;  // k-steps of S^T
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  bf16* smem = reinterpret_cast<bf16*>(smem_raw);
+  constexpr int NDB = D / 32;
+  constexpr int NKS = D / 16;
+  __shared__ __attribute__((aligned(16))) bf16 k0s[C::TILE], v0s[C::TILE], k1s[C::TILE], v1s[C::TILE];
+  lds_t<bf16>* K0 = (lds_t<bf16>*)k0s;
+  lds_t<bf16>* V0 = (lds_t<bf16>*)v0s;
+  lds_t<bf16>* K1 = (lds_t<bf16>*)k1s;
+  lds_t<bf16>* V1 = (lds_t<bf16>*)v1s;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int T = p.T, H = p.H, W = p.window;
@@ -154,6 +214,9 @@ __global__ void __launch_bounds__(256) fwd_bf16_kernel(Params p) {
   const int bh = L / p.nqb;
   const int qb = p.nqb - 1 - (L - bh * p.nqb);
   const int b = bh / H, h = bh - b * H;
+  const size_t head0 = ((size_t)b * T * H + h) * D;   // element (b, 0, h, 0)
+  const bf16* kbase = p.k + head0;
+  const bf16* vbase = p.v + head0;
 
   const int q0 = qb * BM;
   const int qw = q0 + wave * 32;      // first query of this wave
@@ -162,7 +225,7 @@ __global__ void __launch_bounds__(256) fwd_bf16_kernel(Params p) {
   // Q^T operand: 8 bf16 of row myq per k-step, held for the whole kernel.
   bf16x8 qreg[NKS];
   {
-    const bf16* qp = p.q + (((size_t)b * T + min(myq, T - 1)) * H + h) * D + 8 * hi;
+    const bf16* qp = p.q + head0 + (size_t)min(myq, T - 1) * H * D + 8 * hi;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       uint4 w = *reinterpret_cast<const uint4*>(qp + 16 * ks);
@@ -174,108 +237,44 @@ __global__ void __launch_bounds__(256) fwd_bf16_kernel(Params p) {
   const int kt_lo = max(0, q0 - W + 1) / BN;
   const int kt_hi = min(T - 1, q0 + BM - 1) / BN;
 
-  f32x16 oacc[NDB];
+  WaveState<D> ws;
 #pragma unroll
-  for (int i = 0; i < NDB; ++i) oacc[i] = (f32x16){};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int i = 0; i < NDB; ++i) ws.oacc[i] = (f32x16){};
+  ws.m_ref = -INFINITY;
+  ws.l_run = 0.f;
 
-  Stage<D, GATE> st;
-  st.load(p, b, h, kt_lo, tid);
-  st.store(smem, tid);
+  using TL = Tiles<D, GATE>;
+  TL::load(p, kbase, vbase, K0, V0, kt_lo, wave, lane, tid);
+  wait_vmem();
   __syncthreads();
-
-  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-    const int cur = (kt - kt_lo) & 1;
-    const bool has_next = kt < kt_hi;
-    if (has_next) st.load(p, b, h, kt + 1, tid);
-
-    const bf16* ks = smem + cur * C::BUF_ELEMS;
-    const bf16* vs = ks + C::K_ELEMS;
-    const int k0 = kt * BN;
-    // wave-uniform skip / mask decisions
-    const bool skip = (k0 > qw + 31) || (k0 + BN - 1 < qw - W + 1);
-    if (!skip) {
-      const bool need_mask = (k0 + BN - 1 > qw) || (k0 < qw + 31 - W + 1) || (k0 + BN > T);
-      f32x16 s[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = (f32x16){};
-        const bf16* arow = ks + (kb * 32 + l32) * C::KP + 8 * hi;
-#pragma unroll
-        for (int kk = 0; kk < NKS; ++kk) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + 16 * kk);
-          s[kb] = mfma32(a, qreg[kk], s[kb]);
-        }
-      }
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kg = k0 + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-            const bool ok = (kg <= myq) && (kg > myq - W) && (kg < T);
-            s[kb][i] = ok ? s[kb][i] : -INFINITY;
-          }
-      }
-      float mx = s[0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      mx = fmaxf(mx, half_swap(mx));
-      const float m_new = fmaxf(m_run, mx * p.c);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      float lsum = 0.f;
-      bf16x8 pb[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int sp = 0; sp < 2; ++sp) {
-          float e[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            e[j] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * sp + j], p.c, -m_use));
-            lsum += e[j];
-          }
-#pragma unroll
-          for (int j = 0; j < 8; ++j) pb[kb][sp][j] = (bf16)e[j];
-        }
-      l_run = fmaf(l_run, alpha, lsum);
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const bf16* vrow = vs + (db * 32 + l32) * C::VP + 8 * hi;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int sp = 0; sp < 2; ++sp) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(vrow + kb * 32 + sp * 16);
-            oacc[db] = mfma32(a, pb[kb][sp], oacc[db]);
-          }
-      }
-    }
-    if (has_next) st.store(smem + (cur ^ 1) * C::BUF_ELEMS, tid);
+  // Two tiles per trip so that each LDS buffer is named statically.
+  for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
+    if (kt + 1 <= kt_hi) TL::load(p, kbase, vbase, K1, V1, kt + 1, wave, lane, tid);
+    tile_step<D>(ws, qreg, K0, V0, kt * BN, qw, myq, T, W, p.c, lane);
+    wait_vmem();
+    __syncthreads();
+    if (kt + 1 > kt_hi) break;
+    if (kt + 2 <= kt_hi) TL::load(p, kbase, vbase, K0, V0, kt + 2, wave, lane, tid);
+    tile_step<D>(ws, qreg, K1, V1, (kt + 1) * BN, qw, myq, T, W, p.c, lane);
+    wait_vmem();
     __syncthreads();
   }
 
   // Epilogue: combine the two half-wave partial sums, normalise, store O and lse.
-  const float l_tot = l_run + half_swap(l_run);
+  const float l_tot = ws.l_run + half_swap(ws.l_run);
   const float inv = 1.0f / l_tot;
   if (myq < T) {
-    bf16* op = p.o + (((size_t)b * T + myq) * H + h) * D;
+    bf16* op = p.o + head0 + (size_t)myq * H * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         uint2 w;
-        w.x = pack_bf2(oacc[db][4 * a + 0] * inv, oacc[db][4 * a + 1] * inv);
-        w.y = pack_bf2(oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv);
+        w.x = pack_bf2(ws.oacc[db][4 * a + 0] * inv, ws.oacc[db][4 * a + 1] * inv);
+        w.y = pack_bf2(ws.oacc[db][4 * a + 2] * inv, ws.oacc[db][4 * a + 3] * inv);
         *reinterpret_cast<uint2*>(op + db * 32 + 8 * a + 4 * hi) = w;
       }
-    if (hi == 0) p.lse[((size_t)b * H + h) * T + myq] = (m_run + __log2f(l_tot)) * kLn2;
+    if (hi == 0) p.lse[((size_t)b * H + h) * T + myq] = (ws.m_ref + __log2f(l_tot)) * kLn2;
   }
 }
 
@@ -329,20 +328,14 @@ template <int D, bool GATE>
 static hipError_t launch_fwd_bf16_t(const AttnShape& a, const void* q, const void* k, const void* v,
                                     const void* ve, const float* gate, void* o, float* lse,
                                     hipStream_t s) {
-  using C = fwdk::Cfg<D>;
   fwdk::Params p;
   p.q = (const bf16*)q; p.k = (const bf16*)k; p.v = (const bf16*)v; p.ve = (const bf16*)ve;
   p.gate = gate; p.o = (bf16*)o; p.lse = lse;
   p.B = a.B; p.T = a.T; p.H = a.H; p.window = a.window;
   p.nqb = (a.T + fwdk::BM - 1) / fwdk::BM;
   p.c = a.scale * kLog2e;
-  const size_t smem = 2 * C::BUF_ELEMS * sizeof(bf16);
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&fwdk::fwd_bf16_kernel<D, GATE>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-  if (attr != hipSuccess) return attr;
   const unsigned blocks = (unsigned)p.nqb * a.B * a.H;
-  hipLaunchKernelGGL((fwdk::fwd_bf16_kernel<D, GATE>), dim3(blocks), dim3(256), smem, s, p);
+  hipLaunchKernelGGL((fwdk::fwd_bf16_kernel<D, GATE>), dim3(blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
