@@ -126,8 +126,8 @@ def run_bench(args):
             if cfg["gate"]:
                 ve, gate, dve, dgate = t["ve"], t["gate"], g["dve"], g["dgate"]
             if rec: rec["bwd"][li][0].record()
-            call("swa_bwd_preprocess", P(t["o"]), P(t["dO"]), P(ws), nws, B, T, H, D, sw.SWA_BF16,
-                 stream)
+            call("swa_bwd_preprocess", P(t["o"]), P(t["dO"]), P(t["lse"]), P(ws), nws, B, T, H, D,
+                 sw.SWA_BF16, stream)
             if rec: rec["bwd"][li][1].record()
             call("swa_bwd_main", P(t["qn"]), P(t["kn"]), P(t["v"]), P(ve), P(gate), P(t["lse"]),
                  P(t["dO"]), P(g["dqn"]), P(g["dkn"]), P(g["dv"]), P(dve), P(dgate), P(ws), nws,
@@ -279,7 +279,21 @@ def main():
                     choices=["sssl24", "d24_short", "d24_full", "gpt2_124m", "d24_short_ve"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
+                    help="only run a plain device-to-device copy of this many MiB 5 times (used to "
+                         "scale HBM byte counters under rocprofv3), then exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                          "launches": 5}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; this build measures one GPU "
               "(run with --gpus 1).", file=sys.stderr)

@@ -36,7 +36,7 @@ SIGNATURES = {
     "swa_bwd_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "swa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
                      _I, _I, _I, _I, _I, _F, _I, _P]),
-    "swa_bwd_preprocess": (_I, [_P, _P, _P, _S, _I, _I, _I, _I, _I, _P]),
+    "swa_bwd_preprocess": (_I, [_P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _P]),
     "swa_bwd_main": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
                           _I, _I, _I, _I, _I, _F, _I, _P]),
     "swa_bwd_finalize": (_I, [_P, _P, _S, _I, _I, _I, _I, _I, _P]),
@@ -223,7 +223,8 @@ def swa_bwd_stages(q, k, v, o, lse, dO, window: int, scale: float | None = None,
     else:
         dq, dk, dv, dve, dgate = grads
     st = _stream()
-    _call("swa_bwd_preprocess", _ptr(o), _ptr(dO), _ptr(workspace), nbytes, B, T, H, D, _dt(q), st)
+    _call("swa_bwd_preprocess", _ptr(o), _ptr(dO), _ptr(lse), _ptr(workspace), nbytes, B, T, H, D, _dt(q),
+          st)
     if events is not None:
         events[0].record()
     _call("swa_bwd_main", _ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), _ptr(lse), _ptr(dO),

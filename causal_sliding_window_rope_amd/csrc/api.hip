@@ -213,21 +213,21 @@ int swa_bwd(const void* q, const void* k, const void* v, const void* ve, const f
                     ws_bytes, B, T, H, D, window, scale, dtype, &a));
   const bool bf = dtype == SWA_BF16;
   const hipStream_t s = (hipStream_t)stream;
-  hipError_t e = swa::launch_bwd_pre(a, o, dO, workspace, bf, s);
+  hipError_t e = swa::launch_bwd_pre(a, o, dO, lse, workspace, bf, s);
   if (e == hipSuccess)
     e = swa::launch_bwd_main(a, q, k, v, ve, gate, lse, dO, dq, dk, dv, dve, dgate, workspace, bf, s);
   if (e == hipSuccess) e = swa::launch_bwd_final(a, dq, workspace, bf, s);
   return hip_status(e, fn);
 }
 
-int swa_bwd_preprocess(const void* o, const void* dO, void* workspace, size_t ws_bytes, int B,
-                       int T, int H, int D, swa_dtype dtype, void* stream) {
+int swa_bwd_preprocess(const void* o, const void* dO, const float* lse, void* workspace,
+                       size_t ws_bytes, int B, int T, int H, int D, swa_dtype dtype, void* stream) {
   const char* fn = "swa_bwd_preprocess";
   SWA_TRY(check_shape(fn, B, T, H, D, dtype));
-  SWA_TRY(need(fn, "o", o)); SWA_TRY(need(fn, "dO", dO));
+  SWA_TRY(need(fn, "o", o)); SWA_TRY(need(fn, "dO", dO)); SWA_TRY(need(fn, "lse", lse));
   SWA_TRY(check_ws(fn, workspace, ws_bytes, B, T, H, D, dtype));
   swa::AttnShape a{B, T, H, D, T, 1.f};
-  return hip_status(swa::launch_bwd_pre(a, o, dO, workspace, dtype == SWA_BF16, (hipStream_t)stream), fn);
+  return hip_status(swa::launch_bwd_pre(a, o, dO, lse, workspace, dtype == SWA_BF16, (hipStream_t)stream), fn);
 }
 
 int swa_bwd_main(const void* q, const void* k, const void* v, const void* ve, const float* gate,

@@ -26,12 +26,15 @@
 namespace swa {
 
 // ------------------------------------------------------------------------------------------
-// delta_i = sum_d dO[i, d] * O[i, d]; also zeroes the float32 dQ accumulator row.
+// delta_i = sum_d dO[i, d] * O[i, d] and lse2_i = lse_i * log2(e); also zeroes the float32
+// dQ accumulator row.
 // ------------------------------------------------------------------------------------------
 template <typename E, int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(const E* __restrict__ o,
                                                       const E* __restrict__ dO,
+                                                      const float* __restrict__ lse,
                                                       float* __restrict__ delta,
+                                                      float* __restrict__ lse2,
                                                       float* __restrict__ dq_acc, int rows, int T,
                                                       int H) {
   constexpr int VPT = 16 / sizeof(E), TPR = D / VPT;
@@ -65,7 +68,9 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const E* __restrict__ o,
   }
   if (lr == 0) {
     const int h = row % H, t = (row / H) % T, b = row / (H * T);
-    delta[((size_t)b * H + h) * T + t] = acc;
+    const size_t r = ((size_t)b * H + h) * T + t;
+    delta[r] = acc;
+    lse2[r] = lse[r] * kLog2e;   // log2-domain row terms for the exp2 in the main kernel
   }
 }
 
@@ -89,107 +94,69 @@ constexpr int BNK = 32 * NW;  // keys per workgroup
 constexpr int BMQ = 64;       // queries per tile
 
 template <int D> struct Cfg {
-  static constexpr int QP = D + 8;       // Q / dO tile pitch (row-major)
-  static constexpr int TP = BMQ + 8;     // Q^T / dO^T tile pitch
-  static constexpr int SP = BNK + 8;     // dS tile pitch
-  static constexpr int KTP = BNK + 8;    // K^T pitch
-  static constexpr int OFF_Q = 0;
-  static constexpr int OFF_DO = OFF_Q + BMQ * QP;
-  static constexpr int OFF_QT = OFF_DO + BMQ * QP;
-  static constexpr int OFF_DOT = OFF_QT + D * TP;
-  static constexpr int OFF_DS = OFF_DOT + D * TP;
-  static constexpr int OFF_KT = OFF_DS + BMQ * SP;
-  static constexpr int BF_ELEMS = OFF_KT + D * KTP;
-  static constexpr size_t SMEM = BF_ELEMS * 2 + 2 * BMQ * 4;
-  static constexpr int KG = (D == 128) ? 4 : 2;   // queries per staging unit
-  static constexpr int QGROUPS = BMQ / KG;         // 16 or 32 (x D/8 dgroups = 256 units)
+  static constexpr int CH = D / 8;            // 16-byte chunks per row
+  static constexpr int RPI = 64 / CH;         // rows per 1 KiB wave load
+  static constexpr int QTILE = BMQ * D;       // elements of a Q or dO tile
+  static constexpr int NIQ = BMQ / RPI / NW;  // wave loads per tile per wave
+  static constexpr int NIK = BNK / RPI / NW;  // wave loads of the K block per wave
+  static constexpr int ST = BNK * BMQ;        // dS^T tile elements ([key][query], 128-byte rows)
 };
-
-__device__ __forceinline__ int tpos(int q) {  // bits 2 and 3 swapped (see fwd.hip)
-  return (q & ~12) | ((q & 4) << 1) | ((q & 8) >> 1);
-}
 
 struct Params {
   const bf16* q; const bf16* k; const bf16* v; const bf16* ve; const float* gate;
-  const float* lse; const float* delta; const bf16* dO;
+  const float* lse2; const float* delta; const bf16* dO;
   float* dq_acc; bf16* dk; bf16* dv; bf16* dve; float* dgate;
   int B, T, H, window, nkb;
   float c;       // scale * log2(e)
   float scale;
 };
 
+// Asynchronous loads of query tile qt (Q, dO rows and the lse2 / delta row terms) into LDS.
 template <int D>
-struct QStage {
+__device__ __forceinline__ void load_qtile(const Params& p, const bf16* qbase, const bf16* obase,
+                                           const float* l2base, const float* dlbase,
+                                           lds_t<bf16>* Qs, lds_t<bf16>* Os, lds_t<float>* Ls,
+                                           lds_t<float>* Dls, int qt, int wave, int lane) {
   using C = Cfg<D>;
-  uint4 qw[C::KG], ow[C::KG];
-  float l2, dl;
-  __device__ __forceinline__ void load(const Params& p, int b, int h, int qt, int tid) {
-    const int qgrp = tid % C::QGROUPS, dgrp = tid / C::QGROUPS;
+  const size_t rs = (size_t)p.H * D;
 #pragma unroll
-    for (int j = 0; j < C::KG; ++j) {
-      const int qg = qt * BMQ + qgrp * C::KG + j;
-      if (qg < p.T) {
-        const size_t off = (((size_t)b * p.T + qg) * p.H + h) * D + dgrp * 8;
-        qw[j] = *reinterpret_cast<const uint4*>(p.q + off);
-        ow[j] = *reinterpret_cast<const uint4*>(p.dO + off);
-      } else {
-        qw[j] = make_uint4(0, 0, 0, 0);
-        ow[j] = make_uint4(0, 0, 0, 0);
-      }
-    }
-    if (tid < BMQ) {
-      const int qg = qt * BMQ + tid;
-      const size_t r = ((size_t)b * p.H + h) * p.T + qg;
-      l2 = qg < p.T ? p.lse[r] * kLog2e : 0.f;
-      dl = qg < p.T ? p.delta[r] : 0.f;
-    }
+  for (int i = 0; i < C::NIQ; ++i) {
+    const int I = wave * C::NIQ + i;
+    const int r = I * C::RPI + lane / C::CH;
+    const int c = (lane % C::CH) ^ swz<D>(r);
+    const size_t goff = (size_t)min(qt * BMQ + r, p.T - 1) * rs + 8 * c;
+    g2lds16(qbase + goff, Qs + I * C::RPI * D);
+    g2lds16(obase + goff, Os + I * C::RPI * D);
   }
-  __device__ __forceinline__ void store(unsigned char* smem, int tid) const {
-    bf16* sb = reinterpret_cast<bf16*>(smem);
-    float* sf = reinterpret_cast<float*>(smem + C::BF_ELEMS * 2);
-    const int qgrp = tid % C::QGROUPS, dgrp = tid / C::QGROUPS;
-#pragma unroll
-    for (int j = 0; j < C::KG; ++j) {
-      const int ql = qgrp * C::KG + j;
-      *reinterpret_cast<uint4*>(sb + C::OFF_Q + ql * C::QP + dgrp * 8) = qw[j];
-      *reinterpret_cast<uint4*>(sb + C::OFF_DO + ql * C::QP + dgrp * 8) = ow[j];
-    }
-    const int pos = tpos(qgrp * C::KG);
-    transpose_store(sb + C::OFF_QT, qw, dgrp, pos);
-    transpose_store(sb + C::OFF_DOT, ow, dgrp, pos);
-    if (tid < BMQ) { sf[tid] = l2; sf[BMQ + tid] = dl; }
+  if (lane < BMQ / 4) {
+    // a tile that runs past the sequence end reads into the next head's row or the workspace
+    // slack (see bwd_workspace_bytes); those queries are masked
+    if (wave == 0) g2lds16(l2base + qt * BMQ + 4 * lane, (lds_t<bf16>*)Ls);
+    if (wave == 1) g2lds16(dlbase + qt * BMQ + 4 * lane, (lds_t<bf16>*)Dls);
   }
-  __device__ __forceinline__ static void transpose_store(bf16* base, const uint4* w, int dgrp,
-                                                         int pos) {
-    uint32_t u[C::KG][4];
-#pragma unroll
-    for (int j = 0; j < C::KG; ++j) { u[j][0] = w[j].x; u[j][1] = w[j].y; u[j][2] = w[j].z; u[j][3] = w[j].w; }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      bf16* dst = base + (dgrp * 8 + e) * C::TP + pos;
-      // 16-bit element e of each row j
-      auto el = [&](int j) -> uint32_t { return (e & 1) ? (u[j][e >> 1] >> 16) : (u[j][e >> 1] & 0xffffu); };
-      if constexpr (C::KG == 4) {
-        uint2 o;
-        o.x = el(0) | (el(1) << 16);
-        o.y = el(2) | (el(3) << 16);
-        *reinterpret_cast<uint2*>(dst) = o;
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = el(0) | (el(1) << 16);
-      }
-    }
-  }
-};
+}
 
 template <int D, bool GATE>
-__global__ void __launch_bounds__(256) bwd_bf16_kernel(Params p) {
+__global__ void __launch_bounds__(256, 1) bwd_bf16_kernel(Params p) {
   using C = Cfg<D>;
   constexpr int NDB = D / 32, NKS = D / 16;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  bf16* sb = reinterpret_cast<bf16*>(smem);
-  const float* sf = reinterpret_cast<const float*>(smem + C::BF_ELEMS * 2);
+  __shared__ __attribute__((aligned(16))) bf16 ks_[BNK * D], vs_[BNK * D], q0_[C::QTILE],
+      q1_[C::QTILE], o0_[C::QTILE], o1_[C::QTILE], st_[C::ST];
+  __shared__ __attribute__((aligned(16))) float l0_[BMQ], l1_[BMQ], d0_[BMQ], d1_[BMQ];
+  lds_t<bf16>* Ks = (lds_t<bf16>*)ks_;
+  lds_t<bf16>* Vs = (lds_t<bf16>*)vs_;
+  lds_t<bf16>* Q0 = (lds_t<bf16>*)q0_;
+  lds_t<bf16>* Q1 = (lds_t<bf16>*)q1_;
+  lds_t<bf16>* O0 = (lds_t<bf16>*)o0_;
+  lds_t<bf16>* O1 = (lds_t<bf16>*)o1_;
+  lds_t<bf16>* ST = (lds_t<bf16>*)st_;
+  lds_t<float>* L0 = (lds_t<float>*)l0_;
+  lds_t<float>* L1 = (lds_t<float>*)l1_;
+  lds_t<float>* D0 = (lds_t<float>*)d0_;
+  lds_t<float>* D1 = (lds_t<float>*)d1_;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int g = lane >> 4, j = lane & 15;
   const int T = p.T, H = p.H, W = p.window;
 
   const int nblk = gridDim.x;
@@ -198,52 +165,43 @@ __global__ void __launch_bounds__(256) bwd_bf16_kernel(Params p) {
   const int bh = L / p.nkb;
   const int kbk = L - bh * p.nkb;
   const int b = bh / H, h = bh - b * H;
+  const size_t head0 = ((size_t)b * T * H + h) * D;
+  const size_t rs = (size_t)H * D;
   const int kb0 = kbk * BNK;
   const int kw = kb0 + 32 * wave;
   const int mykey = kw + l32;
+  const bf16* qbase = p.q + head0;
+  const bf16* obase = p.dO + head0;
+  const float* l2base = p.lse2 + (size_t)bh * T;
+  const float* dlbase = p.delta + (size_t)bh * T;
 
-  // B operands: this lane's key row of K and of v_eff, 8 dims per k-step.
-  bf16x8 kreg[NKS], vreg[NKS];
-  float gk = 0.f;
-  {
-    const size_t row = ((size_t)b * T + min(mykey, T - 1)) * H + h;
-    const bool ok = mykey < T;
-    if constexpr (GATE) gk = ok ? p.gate[row] : 0.f;
+  // K and v_eff rows of the workgroup's key block into LDS (row-major, swizzled). K is the B
+  // operand of S = Q K^T (128-bit row reads) and of dQ = dS K (transposing reads); v_eff is the
+  // B operand of dP = dO V^T.
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const size_t off = row * D + 16 * ks + 8 * hi;
-      uint4 kk = *reinterpret_cast<const uint4*>(p.k + off);
-      uint4 vv = *reinterpret_cast<const uint4*>(p.v + off);
-      if constexpr (GATE) {
-        const uint4 ee = *reinterpret_cast<const uint4*>(p.ve + off);
-        vv.x = pack_bf2(fmaf(gk, bf_lo(ee.x), bf_lo(vv.x)), fmaf(gk, bf_hi(ee.x), bf_hi(vv.x)));
-        vv.y = pack_bf2(fmaf(gk, bf_lo(ee.y), bf_lo(vv.y)), fmaf(gk, bf_hi(ee.y), bf_hi(vv.y)));
-        vv.z = pack_bf2(fmaf(gk, bf_lo(ee.z), bf_lo(vv.z)), fmaf(gk, bf_hi(ee.z), bf_hi(vv.z)));
-        vv.w = pack_bf2(fmaf(gk, bf_lo(ee.w), bf_lo(vv.w)), fmaf(gk, bf_hi(ee.w), bf_hi(vv.w)));
-      }
-      if (!ok) { kk = make_uint4(0, 0, 0, 0); vv = make_uint4(0, 0, 0, 0); }
-      kreg[ks] = __builtin_bit_cast(bf16x8, kk);
-      vreg[ks] = __builtin_bit_cast(bf16x8, vv);
-    }
+  for (int i = 0; i < C::NIK; ++i) {
+    const int I = wave * C::NIK + i;
+    const int r = I * C::RPI + lane / C::CH;
+    const int c = (lane % C::CH) ^ swz<D>(r);
+    const size_t goff = head0 + (size_t)min(kb0 + r, T - 1) * rs + 8 * c;
+    g2lds16(p.k + goff, Ks + I * C::RPI * D);
+    if constexpr (!GATE) g2lds16(p.v + goff, Vs + I * C::RPI * D);
   }
-  // K^T of the whole key block into LDS (B operand of dQ = dS K): KT[d][key].
-  for (int u = tid; u < (BNK / 4) * (D / 8); u += 256) {
-    const int kg4 = u % (BNK / 4), dgrp = u / (BNK / 4);
-    uint32_t w[4][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = kb0 + kg4 * 4 + j;
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (key < T) x = *reinterpret_cast<const uint4*>(p.k + (((size_t)b * T + key) * H + h) * D + dgrp * 8);
-      w[j][0] = x.x; w[j][1] = x.y; w[j][2] = x.z; w[j][3] = x.w;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      auto el = [&](int j) -> uint32_t { return (e & 1) ? (w[j][e >> 1] >> 16) : (w[j][e >> 1] & 0xffffu); };
-      uint2 o;
-      o.x = el(0) | (el(1) << 16);
-      o.y = el(2) | (el(3) << 16);
-      *reinterpret_cast<uint2*>(sb + C::OFF_KT + (dgrp * 8 + e) * C::KTP + kg4 * 4) = o;
+  if constexpr (GATE) {
+    for (int id = tid; id < BNK * C::CH; id += 256) {
+      const int r = id / C::CH, pos = id % C::CH;
+      const int c = pos ^ swz<D>(r);
+      const int row = min(kb0 + r, T - 1);
+      const size_t goff = head0 + (size_t)row * rs + 8 * c;
+      const uint4 a = *reinterpret_cast<const uint4*>(p.v + goff);
+      const uint4 e = *reinterpret_cast<const uint4*>(p.ve + goff);
+      const float gk = p.gate[(size_t)(b * T + row) * H + h];
+      u32x4 o;
+      o.x = pack_bf2(fmaf(gk, bf_lo(e.x), bf_lo(a.x)), fmaf(gk, bf_hi(e.x), bf_hi(a.x)));
+      o.y = pack_bf2(fmaf(gk, bf_lo(e.y), bf_lo(a.y)), fmaf(gk, bf_hi(e.y), bf_hi(a.y)));
+      o.z = pack_bf2(fmaf(gk, bf_lo(e.z), bf_lo(a.z)), fmaf(gk, bf_hi(e.z), bf_hi(a.z)));
+      o.w = pack_bf2(fmaf(gk, bf_lo(e.w), bf_lo(a.w)), fmaf(gk, bf_hi(e.w), bf_hi(a.w)));
+      *reinterpret_cast<lds_t<u32x4>*>(Vs + r * D + 8 * pos) = o;
     }
   }
 
@@ -254,115 +212,169 @@ __global__ void __launch_bounds__(256) bwd_bf16_kernel(Params p) {
   const int qt_lo = kb0 / BMQ;
   const int qt_hi = min(T - 1, kb0 + BNK - 1 + W - 1) / BMQ;
 
-  QStage<D> st;
-  st.load(p, b, h, qt_lo, tid);
-  st.store(smem, tid);
-  __syncthreads();
+  // Lane-constant LDS element offsets. Every swizzled address below is one of these plus a
+  // compile-time row offset, so the LDS loads use immediate offsets off a few registers.
+  const int jr = j >> 2, jc = j & 3;
+  // (a) 128-bit row reads, row (32 mb + l32) of a [rows][D] tile, chunk 2 ks + hi
+  int rowb[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) rowb[ks] = l32 * D + 8 * ((2 * ks + hi) ^ swz<D>(l32));
+  const int kvrow = 32 * wave * D;  // this wave's key rows in the K / V blocks
+  // (b) transposing reads of a [rows][D] tile: rows 4 hi + jr (+8) (+ 32 mb + 16 sp), d-block db
+  int trb1[NDB], trb2[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int d = 32 * db + 16 * (g & 1) + 4 * jc;
+    const int r1 = 4 * hi + jr, r2 = r1 + 8;
+    trb1[db] = r1 * D + 8 * ((d >> 3) ^ swz<D>(r1)) + 4 * ((d >> 2) & 1);
+    trb2[db] = r2 * D + 8 * ((d >> 3) ^ swz<D>(r2)) + 4 * ((d >> 2) & 1);
+  }
+  // (c) dQ: transposing reads of dS^T ([key][query], 128-byte rows) and of the K block
+  constexpr int NMB = (D == 128) ? 2 : 1;
+  const int dq_db = (D == 128) ? wave : (wave & 1);
+  int stb1[NMB], stb2[NMB];
+#pragma unroll
+  for (int jm = 0; jm < NMB; ++jm) {
+    const int mb = (D == 128) ? jm : (wave >> 1);
+    const int qc = 32 * mb + 16 * (g & 1) + 4 * jc;
+    const int k1 = 8 * hi + jr, k2 = k1 + 4;
+    stb1[jm] = k1 * BMQ + 8 * ((qc >> 3) ^ swz<64>(k1)) + 4 * ((qc >> 2) & 1);
+    stb2[jm] = k2 * BMQ + 8 * ((qc >> 3) ^ swz<64>(k2)) + 4 * ((qc >> 2) & 1);
+  }
+  int kqb1, kqb2;
+  {
+    const int dc = 32 * dq_db + 16 * (g & 1) + 4 * jc;
+    const int k1 = 8 * hi + jr, k2 = k1 + 4;
+    kqb1 = k1 * D + 8 * ((dc >> 3) ^ swz<D>(k1)) + 4 * ((dc >> 2) & 1);
+    kqb2 = k2 * D + 8 * ((dc >> 3) ^ swz<D>(k2)) + 4 * ((dc >> 2) & 1);
+  }
+  // (d) this lane's dS^T row and its 8-byte slot
+  const int kl = 32 * wave + l32;
+  const int stw = kl * BMQ + 4 * hi;
+  const int stsw = swz<64>(kl);
+  // dQ accumulator: this lane's column for query row (q0 + 4 hi) of the tile
+  float* const dqcol = p.dq_acc + head0 + (size_t)(4 * hi) * rs + dq_db * 32 + l32;
 
-  for (int qt = qt_lo; qt <= qt_hi; ++qt) {
-    const bool has_next = qt < qt_hi;
-    if (has_next) st.load(p, b, h, qt + 1, tid);
+  // One query tile: recompute S, P, dP, dS; accumulate dV, dK; dS^T to LDS; dQ slice -> atomics.
+  auto tile = [&](const lds_t<bf16>* Qs, const lds_t<bf16>* Os, const lds_t<float>* Ls,
+                  const lds_t<float>* Dls, int qt) {
     const int q0 = qt * BMQ;
     const bool skip = (q0 + BMQ - 1 < kw) || (q0 > kw + 31 + W - 1) || (kw >= T);
     if (!skip) {
       const bool need_mask = (q0 < kw + 31) || (q0 + BMQ - 1 > kw + W - 1) || (q0 + BMQ > T) ||
                              (kw + 32 > T);
-      f32x16 s[2], dp[2];
+      // the two 32-query halves of the tile one after the other (halves the live registers)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        s[mb] = (f32x16){};
-        dp[mb] = (f32x16){};
-        const bf16* qrow = sb + C::OFF_Q + (mb * 32 + l32) * C::QP + 8 * hi;
-        const bf16* orow = sb + C::OFF_DO + (mb * 32 + l32) * C::QP + 8 * hi;
+        f32x16 s = (f32x16){}, dp = (f32x16){};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-          s[mb] = mfma32(*reinterpret_cast<const bf16x8*>(qrow + 16 * ks), kreg[ks], s[mb]);
-          dp[mb] = mfma32(*reinterpret_cast<const bf16x8*>(orow + 16 * ks), vreg[ks], dp[mb]);
+          const int off = mb * 32 * D + rowb[ks];
+          const bf16x8 aq = *reinterpret_cast<const lds_t<bf16x8>*>(Qs + off);
+          const bf16x8 bk = *reinterpret_cast<const lds_t<bf16x8>*>(Ks + kvrow + rowb[ks]);
+          const bf16x8 ao = *reinterpret_cast<const lds_t<bf16x8>*>(Os + off);
+          const bf16x8 bv = *reinterpret_cast<const lds_t<bf16x8>*>(Vs + kvrow + rowb[ks]);
+          s = mfma32(aq, bk, s);
+          dp = mfma32(ao, bv, dp);
         }
-      }
-      bf16x8 pb[2][2], sbf[2][2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+        sched_fence();
+        bf16x8 pb[2], sbf[2];
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           const int ql = mb * 32 + 8 * a + 4 * hi;  // first of 4 consecutive queries
-          const float4 l2 = *reinterpret_cast<const float4*>(sf + ql);
-          const float4 dl = *reinterpret_cast<const float4*>(sf + BMQ + ql);
-          const float l2v[4] = {l2.x, l2.y, l2.z, l2.w};
-          const float dlv[4] = {dl.x, dl.y, dl.z, dl.w};
+          const f32x4 l2 = *reinterpret_cast<const lds_t<f32x4>*>(Ls + ql);
+          const f32x4 dl = *reinterpret_cast<const lds_t<f32x4>*>(Dls + ql);
+          float pv[4], dsv[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = 4 * a + r;
-            float pv = __builtin_amdgcn_exp2f(fmaf(s[mb][i], p.c, -l2v[r]));
+            pv[r] = __builtin_amdgcn_exp2f(fmaf(s[i], p.c, -l2[r]));
             if (need_mask) {
               const int qg = q0 + ql + r;
               const bool ok = (mykey <= qg) && (mykey > qg - W) && (qg < T) && (mykey < T);
-              pv = ok ? pv : 0.f;
+              pv[r] = ok ? pv[r] : 0.f;
             }
-            const float ds = pv * (dp[mb][i] - dlv[r]);
-            pb[mb][i >> 3][i & 7] = (bf16)pv;
-            sbf[mb][i >> 3][i & 7] = (bf16)ds;
+            dsv[r] = pv[r] * (dp[i] - dl[r]);
           }
+          const bf16x2 p01 = __builtin_convertvector((f32x2){pv[0], pv[1]}, bf16x2);
+          const bf16x2 p23 = __builtin_convertvector((f32x2){pv[2], pv[3]}, bf16x2);
+          const bf16x2 d01 = __builtin_convertvector((f32x2){dsv[0], dsv[1]}, bf16x2);
+          const bf16x2 d23 = __builtin_convertvector((f32x2){dsv[2], dsv[3]}, bf16x2);
+          const int e0 = 4 * (a & 1);
+          pb[a >> 1][e0] = p01[0]; pb[a >> 1][e0 + 1] = p01[1];
+          pb[a >> 1][e0 + 2] = p23[0]; pb[a >> 1][e0 + 3] = p23[1];
+          sbf[a >> 1][e0] = d01[0]; sbf[a >> 1][e0 + 1] = d01[1];
+          sbf[a >> 1][e0 + 2] = d23[0]; sbf[a >> 1][e0 + 3] = d23[1];
+          // dS^T row kl, queries ql..ql+3 (8 bytes); chunk (4 mb + a) of the row
+          const bf16x4 w4 = {d01[0], d01[1], d23[0], d23[1]};
+          *reinterpret_cast<lds_t<bf16x4>*>(ST + stw + 8 * ((4 * mb + a) ^ stsw)) = w4;
         }
-      }
+        // dV += P^T dO and dK += dS^T Q; B operands by transposing reads of the row-major tiles.
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const bf16* otr = sb + C::OFF_DOT + (db * 32 + l32) * C::TP + 8 * hi;
-        const bf16* qtr = sb + C::OFF_QT + (db * 32 + l32) * C::TP + 8 * hi;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int db = 0; db < NDB; ++db) {
 #pragma unroll
           for (int sp = 0; sp < 2; ++sp) {
-            dv[db] = mfma32(pb[mb][sp], *reinterpret_cast<const bf16x8*>(otr + mb * 32 + sp * 16), dv[db]);
-            dk[db] = mfma32(sbf[mb][sp], *reinterpret_cast<const bf16x8*>(qtr + mb * 32 + sp * 16), dk[db]);
+            const int ro = (mb * 32 + sp * 16) * D;
+            const bf16x8 bo = __builtin_shufflevector(ds_read_tr16(Os + ro + trb1[db]),
+                                                      ds_read_tr16(Os + ro + trb2[db]),
+                                                      0, 1, 2, 3, 4, 5, 6, 7);
+            const bf16x8 bq = __builtin_shufflevector(ds_read_tr16(Qs + ro + trb1[db]),
+                                                      ds_read_tr16(Qs + ro + trb2[db]),
+                                                      0, 1, 2, 3, 4, 5, 6, 7);
+            dv[db] = mfma32(pb[sp], bo, dv[db]);
+            dk[db] = mfma32(sbf[sp], bq, dk[db]);
           }
-      }
-      // dS (queries x keys) into LDS for the dQ contraction
-      bf16* dsw = sb + C::OFF_DS + 32 * wave + l32;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int ql = mb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-          dsw[ql * C::SP] = sbf[mb][i >> 3][i & 7];
+          sched_fence();
         }
+      }
     } else {
-      // this wave's keys see none of the tile: zero its dS columns
-      for (int r = lane; r < BMQ * 4; r += 64) {
-        const int ql = r >> 2, c = r & 3;
-        *reinterpret_cast<uint4*>(sb + C::OFF_DS + ql * C::SP + 32 * wave + 8 * c) = make_uint4(0, 0, 0, 0);
-      }
+      // this wave's keys see none of the tile: zero its dS^T rows
+      for (int r = lane; r < 32 * (BMQ / 8); r += 64)
+        *reinterpret_cast<lds_t<u32x4>*>(ST + (32 * wave + (r >> 3)) * BMQ + 8 * (r & 7)) =
+            (u32x4){0u, 0u, 0u, 0u};
     }
     __syncthreads();
-    // dQ slice: D=128 -> wave owns d-block `wave`, both 32-query halves; D=64 -> d-block
-    // (wave & 1), query half (wave >> 1).
-    {
-      constexpr int NMB = (D == 128) ? 2 : 1;
-      const int db = (D == 128) ? wave : (wave & 1);
+    // dQ slice: D=128 -> wave owns d-block `wave` for both 32-query halves; D=64 -> d-block
+    // (wave & 1) for query half (wave >> 1). A = dS (from dS^T), B = K, both transposing reads.
 #pragma unroll
-      for (int j = 0; j < NMB; ++j) {
-        const int mb = (D == 128) ? j : (wave >> 1);
-        f32x16 acc = (f32x16){};
-        const bf16* arow = sb + C::OFF_DS + (mb * 32 + l32) * C::SP + 8 * hi;
-        const bf16* brow = sb + C::OFF_KT + (db * 32 + l32) * C::KTP + 8 * hi;
+    for (int jm = 0; jm < NMB; ++jm) {
+      const int mb = (D == 128) ? jm : (wave >> 1);
+      f32x16 acc = (f32x16){};
 #pragma unroll
-        for (int ks = 0; ks < BNK / 16; ++ks)
-          acc = mfma32(*reinterpret_cast<const bf16x8*>(arow + 16 * ks),
-                       *reinterpret_cast<const bf16x8*>(brow + 16 * ks), acc);
+      for (int ks = 0; ks < BNK / 16; ++ks) {
+        const bf16x8 a = __builtin_shufflevector(ds_read_tr16(ST + 16 * ks * BMQ + stb1[jm]),
+                                                 ds_read_tr16(ST + 16 * ks * BMQ + stb2[jm]),
+                                                 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 bk = __builtin_shufflevector(ds_read_tr16(Ks + 16 * ks * D + kqb1),
+                                                  ds_read_tr16(Ks + 16 * ks * D + kqb2),
+                                                  0, 1, 2, 3, 4, 5, 6, 7);
+        acc = mfma32(a, bk, acc);
+        if (ks & 1) sched_fence();
+      }
+      // lane owns d = 32 dq_db + l32 of queries q0 + 32 mb + 8(i/4) + 4 hi + (i%4)
+      float* const col = dqcol + (size_t)(q0 + 32 * mb) * rs;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int qg = q0 + mb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-          if (qg < T)
-            unsafeAtomicAdd(p.dq_acc + (((size_t)b * T + qg) * H + h) * D + db * 32 + l32,
-                            acc[i] * p.scale);
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int qr = 8 * (i >> 2) + (i & 3);
+        if (q0 + 32 * mb + 4 * hi + qr < T)
+          unsafeAtomicAdd(col + (size_t)qr * rs, acc[i] * p.scale);
       }
     }
+  };
+
+  load_qtile<D>(p, qbase, obase, l2base, dlbase, Q0, O0, L0, D0, qt_lo, wave, lane);
+  wait_vmem();
+  __syncthreads();
+  for (int qt = qt_lo; qt <= qt_hi; qt += 2) {
+    if (qt + 1 <= qt_hi) load_qtile<D>(p, qbase, obase, l2base, dlbase, Q1, O1, L1, D1, qt + 1, wave, lane);
+    tile(Q0, O0, L0, D0, qt);
+    wait_vmem();
     __syncthreads();
-    if (has_next) {
-      st.store(smem, tid);
-      __syncthreads();
-    }
+    if (qt + 1 > qt_hi) break;
+    if (qt + 2 <= qt_hi) load_qtile<D>(p, qbase, obase, l2base, dlbase, Q0, O0, L0, D0, qt + 2, wave, lane);
+    tile(Q1, O1, L1, D1, qt + 1);
+    wait_vmem();
+    __syncthreads();
   }
 
   // Epilogue: lane owns d = 32 db + l32 of keys kw + 8(i/4) + 4 hi + (i%4).
@@ -370,13 +382,12 @@ __global__ void __launch_bounds__(256) bwd_bf16_kernel(Params p) {
   for (int i = 0; i < 16; ++i) {
     const int key = kw + 8 * (i >> 2) + 4 * hi + (i & 3);
     if (key >= T) continue;
-    const size_t row = ((size_t)b * T + key) * H + h;
-    float gsum = 0.f;
-    float gkey = 0.f;
-    if constexpr (GATE) gkey = p.gate[row];
+    const size_t row = head0 + (size_t)key * rs;
+    float gsum = 0.f, gkey = 0.f;
+    if constexpr (GATE) gkey = p.gate[(size_t)(b * T + key) * H + h];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const size_t off = row * D + db * 32 + l32;
+      const size_t off = row + db * 32 + l32;
       p.dk[off] = (bf16)(dk[db][i] * p.scale);
       p.dv[off] = (bf16)dv[db][i];
       if constexpr (GATE) {
@@ -387,7 +398,7 @@ __global__ void __launch_bounds__(256) bwd_bf16_kernel(Params p) {
     if constexpr (GATE) {
 #pragma unroll
       for (int m = 1; m < 32; m <<= 1) gsum += xor_shfl(gsum, m);
-      if (l32 == 0) p.dgate[row] = gsum;
+      if (l32 == 0) p.dgate[(size_t)(b * T + key) * H + h] = gsum;
     }
   }
 }
@@ -497,58 +508,61 @@ __global__ void __launch_bounds__(64) bwd_dq_f32_kernel(
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Workspace: delta (B,H,T) | lse2 (B,H,T) | [bf16 path] dq accumulator (B,T,H,D) float32. Each
+// block is 256-byte aligned and followed by 512 bytes of slack, so the 16-byte row-term loads of
+// a query tile that runs past the sequence end stay inside the allocation.
+static size_t rowterm_block(int B, int T, int H) {
+  return align256((size_t)B * H * T * sizeof(float)) + 512;
+}
+
 size_t bwd_workspace_bytes(int B, int T, int H, int D, bool bf16) {
-  const size_t delta = align256((size_t)B * H * T * sizeof(float));
   const size_t acc = bf16 ? align256((size_t)B * T * H * D * sizeof(float)) : 0;
-  return delta + acc;
+  return 2 * rowterm_block(B, T, H) + acc;
 }
 
 template <typename E, int D>
-static void launch_pre(const void* o, const void* dO, float* delta, float* dq_acc, int B, int T,
-                       int H, hipStream_t s) {
+static void launch_pre(const void* o, const void* dO, const float* lse, float* delta, float* lse2,
+                       float* dq_acc, int B, int T, int H, hipStream_t s) {
   constexpr int TPR = D / (16 / sizeof(E));
   const int rows = B * T * H;
   const int rpb = 256 / TPR;
   hipLaunchKernelGGL((bwd_pre_kernel<E, D>), dim3((rows + rpb - 1) / rpb), dim3(256), 0, s,
-                     (const E*)o, (const E*)dO, delta, dq_acc, rows, T, H);
+                     (const E*)o, (const E*)dO, lse, delta, lse2, dq_acc, rows, T, H);
 }
 
 template <int D, bool GATE>
 static hipError_t launch_bwd_bf16_t(const AttnShape& a, const bwdk::Params& p, hipStream_t s) {
-  using C = bwdk::Cfg<D>;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&bwdk::bwd_bf16_kernel<D, GATE>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::SMEM);
-  if (attr != hipSuccess) return attr;
   const unsigned blocks = (unsigned)p.nkb * a.B * a.H;
-  hipLaunchKernelGGL((bwdk::bwd_bf16_kernel<D, GATE>), dim3(blocks), dim3(256), C::SMEM, s, p);
+  hipLaunchKernelGGL((bwdk::bwd_bf16_kernel<D, GATE>), dim3(blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 namespace {
 struct WsView {
   float* delta;
+  float* lse2;
   float* dq_acc;  // bf16 path only
 };
 WsView ws_view(void* ws, int B, int T, int H, bool is_bf16) {
   WsView w;
-  w.delta = reinterpret_cast<float*>(ws);
-  w.dq_acc = is_bf16 ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
-                                                align256((size_t)B * H * T * sizeof(float)))
-                     : nullptr;
+  char* base = reinterpret_cast<char*>(ws);
+  const size_t blk = rowterm_block(B, T, H);
+  w.delta = reinterpret_cast<float*>(base);
+  w.lse2 = reinterpret_cast<float*>(base + blk);
+  w.dq_acc = is_bf16 ? reinterpret_cast<float*>(base + 2 * blk) : nullptr;
   return w;
 }
 }  // namespace
 
-hipError_t launch_bwd_pre(const AttnShape& a, const void* o, const void* dO, void* ws,
-                          bool is_bf16, hipStream_t s) {
+hipError_t launch_bwd_pre(const AttnShape& a, const void* o, const void* dO, const float* lse,
+                          void* ws, bool is_bf16, hipStream_t s) {
   const WsView w = ws_view(ws, a.B, a.T, a.H, is_bf16);
   if (is_bf16) {
-    if (a.D == 64) launch_pre<swa::bf16, 64>(o, dO, w.delta, w.dq_acc, a.B, a.T, a.H, s);
-    else launch_pre<swa::bf16, 128>(o, dO, w.delta, w.dq_acc, a.B, a.T, a.H, s);
+    if (a.D == 64) launch_pre<swa::bf16, 64>(o, dO, lse, w.delta, w.lse2, w.dq_acc, a.B, a.T, a.H, s);
+    else launch_pre<swa::bf16, 128>(o, dO, lse, w.delta, w.lse2, w.dq_acc, a.B, a.T, a.H, s);
   } else {
-    if (a.D == 64) launch_pre<float, 64>(o, dO, w.delta, nullptr, a.B, a.T, a.H, s);
-    else launch_pre<float, 128>(o, dO, w.delta, nullptr, a.B, a.T, a.H, s);
+    if (a.D == 64) launch_pre<float, 64>(o, dO, lse, w.delta, w.lse2, nullptr, a.B, a.T, a.H, s);
+    else launch_pre<float, 128>(o, dO, lse, w.delta, w.lse2, nullptr, a.B, a.T, a.H, s);
   }
   return hipGetLastError();
 }
@@ -562,7 +576,7 @@ hipError_t launch_bwd_main(const AttnShape& a, const void* q, const void* k, con
   if (is_bf16) {
     bwdk::Params p;
     p.q = (const bf16*)q; p.k = (const bf16*)k; p.v = (const bf16*)v; p.ve = (const bf16*)ve;
-    p.gate = gate; p.lse = lse; p.delta = w.delta; p.dO = (const bf16*)dO; p.dq_acc = w.dq_acc;
+    p.gate = gate; p.lse2 = w.lse2; p.delta = w.delta; p.dO = (const bf16*)dO; p.dq_acc = w.dq_acc;
     p.dk = (bf16*)dk; p.dv = (bf16*)dv; p.dve = (bf16*)dve; p.dgate = dgate;
     p.B = B; p.T = T; p.H = H; p.window = a.window;
     p.nkb = (T + bwdk::BNK - 1) / bwdk::BNK;

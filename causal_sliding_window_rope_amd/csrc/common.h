@@ -67,10 +67,18 @@ __device__ __forceinline__ bf16x4 ds_read_tr16(const lds_t<bf16>* p) {
   return __builtin_bit_cast(bf16x4, r);
 }
 
-// Bank swizzle of 16-byte chunk positions within a tile row (XOR with a function of the row):
-// keeps the 128-bit row reads of 8 consecutive rows and the transposing reads of 4
-// consecutive rows free of bank conflicts.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// Bank swizzle of 16-byte chunk positions within a tile row of D bf16 (XOR with a function of
+// the row). gfx950 LDS has 64 four-byte banks; a 128-bit read serves 16 lanes per cycle and a
+// transposing 64-bit read 32 lanes per cycle. With these functions the row reads of 16
+// consecutive rows at one chunk, and the transposing reads of 4 consecutive rows x 4 chunks,
+// each touch all 64 banks once (measured: zero SQ_LDS_BANK_CONFLICT).
+template <int D> __device__ __forceinline__ int swz(int r);
+template <> __device__ __forceinline__ int swz<128>(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+template <> __device__ __forceinline__ int swz<64>(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+
+// Scheduling fence: the compiler may not move instructions across it. Used to bound how far
+// ahead LDS loads are hoisted (each hoisted load keeps its result registers live).
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);

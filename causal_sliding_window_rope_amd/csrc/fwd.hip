@@ -67,7 +67,7 @@ struct Tiles {
     for (int i = 0; i < C::NIW; ++i) {
       const int I = wave * C::NIW + i;
       const int r = I * C::RPI + lane / C::CH;
-      const int c = (lane % C::CH) ^ swz(r);
+      const int c = (lane % C::CH) ^ swz<D>(r);
       const size_t goff = (size_t)min(kt * BN + r, T - 1) * rs + 8 * c;
       g2lds16(kbase + goff, ks + I * C::RPI * D);
       if constexpr (!GATE) g2lds16(vbase + goff, vs + I * C::RPI * D);
@@ -78,7 +78,7 @@ struct Tiles {
       for (int j = 0; j < C::CPT; ++j) {
         const int id = tid + 256 * j;
         const int r = id / C::CH, pos = id % C::CH;
-        const int c = pos ^ swz(r);
+        const int c = pos ^ swz<D>(r);
         const int row = min(kt * BN + r, T - 1);
         const size_t goff = (size_t)row * rs + 8 * c;
         const uint4 a = *reinterpret_cast<const uint4*>(vbase + goff);
@@ -118,7 +118,7 @@ __device__ __forceinline__ void tile_step(WaveState<D>& ws, const bf16x8* qreg,
     s[kb] = (f32x16){};
     const int m = kb * 32 + l32;
     const lds_t<bf16>* arow = ks + m * D;
-    const int sw = swz(m);
+    const int sw = swz<D>(m);
 #pragma unroll
     for (int kk = 0; kk < NKS; ++kk) {
       const bf16x8 a = *reinterpret_cast<const lds_t<bf16x8>*>(arow + 8 * ((2 * kk + hi) ^ sw));
@@ -185,8 +185,8 @@ __device__ __forceinline__ void tile_step(WaveState<D>& ws, const bf16x8* qreg,
 #pragma unroll
       for (int sp = 0; sp < 2; ++sp) {
         const int r1 = kb * 32 + sp * 16 + 4 * hi + (j >> 2), r2 = r1 + 8;
-        const bf16x4 lo = ds_read_tr16(vs + r1 * D + 8 * (cc ^ swz(r1)) + 4 * half);
-        const bf16x4 up = ds_read_tr16(vs + r2 * D + 8 * (cc ^ swz(r2)) + 4 * half);
+        const bf16x4 lo = ds_read_tr16(vs + r1 * D + 8 * (cc ^ swz<D>(r1)) + 4 * half);
+        const bf16x4 up = ds_read_tr16(vs + r2 * D + 8 * (cc ^ swz<D>(r2)) + 4 * half);
         const bf16x8 a = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
         ws.oacc[db] = mfma32(a, pb[kb][sp], ws.oacc[db]);
       }

@@ -33,8 +33,8 @@ hipError_t launch_fwd(const AttnShape& a, const void* q, const void* k, const vo
 size_t bwd_workspace_bytes(int B, int T, int H, int D, bool bf16);
 // Backward in three stages on one workspace: row terms (and zeroed dq accumulator), main
 // kernel(s), dq conversion (bf16 path only).
-hipError_t launch_bwd_pre(const AttnShape& a, const void* o, const void* dO, void* ws, bool bf16,
-                          hipStream_t s);
+hipError_t launch_bwd_pre(const AttnShape& a, const void* o, const void* dO, const float* lse,
+                          void* ws, bool bf16, hipStream_t s);
 hipError_t launch_bwd_main(const AttnShape& a, const void* q, const void* k, const void* v,
                            const void* ve, const float* gate, const float* lse, const void* dO,
                            void* dq, void* dk, void* dv, void* dve, float* dgate, void* ws,
