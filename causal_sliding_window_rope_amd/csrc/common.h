@@ -80,6 +80,11 @@ template <> __device__ __forceinline__ int swz<64>(int r) { return (((r >> 1) & 
 // ahead LDS loads are hoisted (each hoisted load keeps its result registers live).
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// Placed first in the body of a rarely taken, wave-uniform branch: an empty volatile asm may not
+// be speculated, so the compiler keeps the branch instead of executing the body unconditionally
+// under a select.
+__device__ __forceinline__ void branch_keep() { asm volatile("" ::: "memory"); }
+
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

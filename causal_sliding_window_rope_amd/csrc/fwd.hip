@@ -54,23 +54,42 @@ constexpr float kRescaleSlack = 8.0f;
 template <int D, bool GATE>
 struct Tiles {
   using C = Cfg<D>;
-  // Issue the asynchronous loads of key tile kt into (ks, vs). Every lane moves one 16-byte
-  // chunk per 1 KiB wave load; lane l of load I lands at row I*RPI + l/CH, position l%CH, and
-  // fetches source chunk (l%CH) ^ swz(row). Rows past the sequence end re-read row T-1 (their
-  // scores are masked).
-  __device__ __forceinline__ static void load(const Params& p, const bf16* kbase, const bf16* vbase,
-                                              lds_t<bf16>* ks, lds_t<bf16>* vs, int kt, int wave,
-                                              int lane, int tid) {
-    const int T = p.T;
-    const size_t rs = (size_t)p.H * D;   // row stride in elements
+  // Lane-constant part of the asynchronous tile loads: lane l of wave load I lands at row
+  // I*RPI + l/CH, position l%CH, and fetches source chunk (l%CH) ^ swz(row).
+  int row[C::NIW];         // tile row of each of this wave's loads
+  unsigned loff[C::NIW];   // byte offset of the fetched chunk within a tile that starts at row 0
+  int ldst[C::NIW];        // LDS element offset of the wave load inside a tile buffer
+  __device__ __forceinline__ void init(int H, int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < C::NIW; ++i) {
       const int I = wave * C::NIW + i;
-      const int r = I * C::RPI + lane / C::CH;
-      const int c = (lane % C::CH) ^ swz<D>(r);
-      const size_t goff = (size_t)min(kt * BN + r, T - 1) * rs + 8 * c;
-      g2lds16(kbase + goff, ks + I * C::RPI * D);
-      if constexpr (!GATE) g2lds16(vbase + goff, vs + I * C::RPI * D);
+      row[i] = I * C::RPI + lane / C::CH;
+      loff[i] = 2u * (unsigned)(row[i] * H * D + 8 * ((lane % C::CH) ^ swz<D>(row[i])));
+      ldst[i] = I * C::RPI * D;
+    }
+  }
+  // Issue the loads of key tile kt into (ks, vs): uniform 64-bit tile base + 32-bit lane offset.
+  // In the last tile, rows past the sequence end re-read row T-1 (their scores are masked).
+  __device__ __forceinline__ void load(const Params& p, const bf16* kbase, const bf16* vbase,
+                                       lds_t<bf16>* ks, lds_t<bf16>* vs, int kt, int tid) const {
+    const int T = p.T;
+    const size_t rs = (size_t)p.H * D;
+    const char* kt0 = reinterpret_cast<const char*>(kbase + (size_t)kt * BN * rs);
+    const char* vt0 = reinterpret_cast<const char*>(vbase + (size_t)kt * BN * rs);
+    if (kt * BN + BN <= T) {
+#pragma unroll
+      for (int i = 0; i < C::NIW; ++i) {
+        g2lds16(kt0 + loff[i], ks + ldst[i]);
+        if constexpr (!GATE) g2lds16(vt0 + loff[i], vs + ldst[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::NIW; ++i) {
+        const int over = max(kt * BN + row[i] - (T - 1), 0);
+        const size_t off = loff[i] - 2 * (size_t)over * rs;
+        g2lds16(kt0 + off, ks + ldst[i]);
+        if constexpr (!GATE) g2lds16(vt0 + off, vs + ldst[i]);
+      }
     }
     if constexpr (GATE) {
       // v_eff = v + gate * ve is formed in fp32 on the way into LDS
@@ -79,17 +98,17 @@ struct Tiles {
         const int id = tid + 256 * j;
         const int r = id / C::CH, pos = id % C::CH;
         const int c = pos ^ swz<D>(r);
-        const int row = min(kt * BN + r, T - 1);
-        const size_t goff = (size_t)row * rs + 8 * c;
+        const int grow = min(kt * BN + r, T - 1);
+        const size_t goff = (size_t)grow * rs + 8 * c;
         const uint4 a = *reinterpret_cast<const uint4*>(vbase + goff);
         const uint4 e = *reinterpret_cast<const uint4*>(p.ve + (vbase - p.v) + goff);
-        const float g = p.gate[(vbase - p.v) / D + (size_t)row * p.H];
-        uint4 o;
+        const float g = p.gate[(vbase - p.v) / D + (size_t)grow * p.H];
+        u32x4 o;
         o.x = pack_bf2(fmaf(g, bf_lo(e.x), bf_lo(a.x)), fmaf(g, bf_hi(e.x), bf_hi(a.x)));
         o.y = pack_bf2(fmaf(g, bf_lo(e.y), bf_lo(a.y)), fmaf(g, bf_hi(e.y), bf_hi(a.y)));
         o.z = pack_bf2(fmaf(g, bf_lo(e.z), bf_lo(a.z)), fmaf(g, bf_hi(e.z), bf_hi(a.z)));
         o.w = pack_bf2(fmaf(g, bf_lo(e.w), bf_lo(a.w)), fmaf(g, bf_hi(e.w), bf_hi(a.w)));
-        *reinterpret_cast<lds_t<u32x4>*>(vs + r * D + 8 * pos) = (u32x4){o.x, o.y, o.z, o.w};
+        *reinterpret_cast<lds_t<u32x4>*>(vs + r * D + 8 * pos) = o;
       }
     }
   }
@@ -126,13 +145,16 @@ __device__ __forceinline__ void tile_step(WaveState<D>& ws, const bf16x8* qreg,
     }
   }
   if (need_mask) {
+    branch_keep();
+    // key k0 + t is visible iff t - lo lies in [0, n): lo, n from the row's window and T
+    const int lo = max(myq - W + 1, 0) - k0 - 4 * hi;
+    const unsigned n = (unsigned)(min(myq, T - 1) - max(myq - W + 1, 0) + 1);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int kg = k0 + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-        const bool ok = (kg <= myq) && (kg > myq - W) && (kg < T);
-        s[kb][i] = ok ? s[kb][i] : -INFINITY;
+        const int t = kb * 32 + 8 * (i >> 2) + (i & 3);   // key offset minus 4*hi
+        s[kb][i] = ((unsigned)(t - lo) < n) ? s[kb][i] : -INFINITY;
       }
   }
   float mx = fmaxf(s[0][0], s[0][1]);
@@ -146,6 +168,7 @@ __device__ __forceinline__ void tile_step(WaveState<D>& ws, const bf16x8* qreg,
   // kRescaleSlack (in log2 units), so exp2(s*c - m_ref) <= 2^8 and the O rescale is rare.
   // Every term of a row is weighted against the same reference, so the result is exact.
   if (__builtin_amdgcn_ballot_w64(mt > ws.m_ref + kRescaleSlack) != 0) {
+    branch_keep();
     const float m_new = fmaxf(ws.m_ref, mt);
     const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(ws.m_ref - m_new);
     ws.l_run *= alpha;
@@ -204,7 +227,8 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(Params p) {
   lds_t<bf16>* K1 = (lds_t<bf16>*)k1s;
   lds_t<bf16>* V1 = (lds_t<bf16>*)v1s;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int T = p.T, H = p.H, W = p.window;
 
   // XCD-aware, longest-first block order.
@@ -243,18 +267,19 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(Params p) {
   ws.m_ref = -INFINITY;
   ws.l_run = 0.f;
 
-  using TL = Tiles<D, GATE>;
-  TL::load(p, kbase, vbase, K0, V0, kt_lo, wave, lane, tid);
+  Tiles<D, GATE> tl;
+  tl.init(H, wave, lane);
+  tl.load(p, kbase, vbase, K0, V0, kt_lo, tid);
   wait_vmem();
   __syncthreads();
   // Two tiles per trip so that each LDS buffer is named statically.
   for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
-    if (kt + 1 <= kt_hi) TL::load(p, kbase, vbase, K1, V1, kt + 1, wave, lane, tid);
+    if (kt + 1 <= kt_hi) tl.load(p, kbase, vbase, K1, V1, kt + 1, tid);
     tile_step<D>(ws, qreg, K0, V0, kt * BN, qw, myq, T, W, p.c, lane);
     wait_vmem();
     __syncthreads();
     if (kt + 1 > kt_hi) break;
-    if (kt + 2 <= kt_hi) TL::load(p, kbase, vbase, K0, V0, kt + 2, wave, lane, tid);
+    if (kt + 2 <= kt_hi) tl.load(p, kbase, vbase, K0, V0, kt + 2, tid);
     tile_step<D>(ws, qreg, K1, V1, (kt + 1) * BN, qw, myq, T, W, p.c, lane);
     wait_vmem();
     __syncthreads();
