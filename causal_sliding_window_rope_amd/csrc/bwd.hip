@@ -155,7 +155,8 @@ __global__ void __launch_bounds__(256, 1) bwd_bf16_kernel(Params p) {
   lds_t<float>* D0 = (lds_t<float>*)d0_;
   lds_t<float>* D1 = (lds_t<float>*)d1_;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int g = lane >> 4, j = lane & 15;
   const int T = p.T, H = p.H, W = p.window;
 
@@ -255,6 +256,9 @@ __global__ void __launch_bounds__(256, 1) bwd_bf16_kernel(Params p) {
   // dQ accumulator: this lane's column for query row (q0 + 4 hi) of the tile
   float* const dqcol = p.dq_acc + head0 + (size_t)(4 * hi) * rs + dq_db * 32 + l32;
 
+  // number of queries (from the key itself on) that see this lane's key: min(W, T - key)
+  const unsigned mask_n = mykey < T ? (unsigned)min(W, T - mykey) : 0u;
+
   // One query tile: recompute S, P, dP, dS; accumulate dV, dK; dS^T to LDS; dQ slice -> atomics.
   auto tile = [&](const lds_t<bf16>* Qs, const lds_t<bf16>* Os, const lds_t<float>* Ls,
                   const lds_t<float>* Dls, int qt) {
@@ -278,26 +282,34 @@ __global__ void __launch_bounds__(256, 1) bwd_bf16_kernel(Params p) {
           dp = mfma32(ao, bv, dp);
         }
         sched_fence();
+        float pv[16];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const f32x4 l2 = *reinterpret_cast<const lds_t<f32x4>*>(Ls + mb * 32 + 8 * a + 4 * hi);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            pv[4 * a + r] = __builtin_amdgcn_exp2f(fmaf(s[4 * a + r], p.c, -l2[r]));
+        }
+        if (need_mask) {
+          branch_keep();
+          // query q0 + mb*32 + 8a + 4hi + r is visible to key `mykey` iff (q - mykey) in [0, n)
+          const int base = q0 + mb * 32 + 4 * hi - mykey;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int t = 8 * (i >> 2) + (i & 3);
+            pv[i] = ((unsigned)(base + t) < mask_n) ? pv[i] : 0.f;
+          }
+        }
         bf16x8 pb[2], sbf[2];
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           const int ql = mb * 32 + 8 * a + 4 * hi;  // first of 4 consecutive queries
-          const f32x4 l2 = *reinterpret_cast<const lds_t<f32x4>*>(Ls + ql);
           const f32x4 dl = *reinterpret_cast<const lds_t<f32x4>*>(Dls + ql);
-          float pv[4], dsv[4];
+          float dsv[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = 4 * a + r;
-            pv[r] = __builtin_amdgcn_exp2f(fmaf(s[i], p.c, -l2[r]));
-            if (need_mask) {
-              const int qg = q0 + ql + r;
-              const bool ok = (mykey <= qg) && (mykey > qg - W) && (qg < T) && (mykey < T);
-              pv[r] = ok ? pv[r] : 0.f;
-            }
-            dsv[r] = pv[r] * (dp[i] - dl[r]);
-          }
-          const bf16x2 p01 = __builtin_convertvector((f32x2){pv[0], pv[1]}, bf16x2);
-          const bf16x2 p23 = __builtin_convertvector((f32x2){pv[2], pv[3]}, bf16x2);
+          for (int r = 0; r < 4; ++r) dsv[r] = pv[4 * a + r] * (dp[4 * a + r] - dl[r]);
+          const bf16x2 p01 = __builtin_convertvector((f32x2){pv[4 * a], pv[4 * a + 1]}, bf16x2);
+          const bf16x2 p23 = __builtin_convertvector((f32x2){pv[4 * a + 2], pv[4 * a + 3]}, bf16x2);
           const bf16x2 d01 = __builtin_convertvector((f32x2){dsv[0], dsv[1]}, bf16x2);
           const bf16x2 d23 = __builtin_convertvector((f32x2){dsv[2], dsv[3]}, bf16x2);
           const int e0 = 4 * (a & 1);
@@ -306,8 +318,9 @@ __global__ void __launch_bounds__(256, 1) bwd_bf16_kernel(Params p) {
           sbf[a >> 1][e0] = d01[0]; sbf[a >> 1][e0 + 1] = d01[1];
           sbf[a >> 1][e0 + 2] = d23[0]; sbf[a >> 1][e0 + 3] = d23[1];
           // dS^T row kl, queries ql..ql+3 (8 bytes); chunk (4 mb + a) of the row
-          const bf16x4 w4 = {d01[0], d01[1], d23[0], d23[1]};
-          *reinterpret_cast<lds_t<bf16x4>*>(ST + stw + 8 * ((4 * mb + a) ^ stsw)) = w4;
+          const unsigned long long w4 = (unsigned long long)__builtin_bit_cast(unsigned, d01) |
+                                        ((unsigned long long)__builtin_bit_cast(unsigned, d23) << 32);
+          ds_store_b64(ST + stw + 8 * ((4 * mb + a) ^ stsw), w4);
         }
         // dV += P^T dO and dK += dS^T Q; B operands by transposing reads of the row-major tiles.
 #pragma unroll
@@ -329,11 +342,10 @@ __global__ void __launch_bounds__(256, 1) bwd_bf16_kernel(Params p) {
       }
     } else {
       // this wave's keys see none of the tile: zero its dS^T rows
-      for (int r = lane; r < 32 * (BMQ / 8); r += 64)
-        *reinterpret_cast<lds_t<u32x4>*>(ST + (32 * wave + (r >> 3)) * BMQ + 8 * (r & 7)) =
-            (u32x4){0u, 0u, 0u, 0u};
+      for (int r = lane; r < 32 * (BMQ / 4); r += 64)
+        ds_store_b64(ST + (32 * wave + (r >> 4)) * BMQ + 4 * (r & 15), 0ull);
     }
-    __syncthreads();
+    lds_sync();
     // dQ slice: D=128 -> wave owns d-block `wave` for both 32-query halves; D=64 -> d-block
     // (wave & 1) for query half (wave >> 1). A = dS (from dS^T), B = K, both transposing reads.
 #pragma unroll
@@ -352,29 +364,36 @@ __global__ void __launch_bounds__(256, 1) bwd_bf16_kernel(Params p) {
         if (ks & 1) sched_fence();
       }
       // lane owns d = 32 dq_db + l32 of queries q0 + 32 mb + 8(i/4) + 4 hi + (i%4)
+      // Every lane issues all 16 atomics (a fixed count per tile, which the wait at the top of
+      // the next tile relies on); rows past the sequence end carry dS = 0, so they add exactly
+      // zero, to row T-1.
       float* const col = dqcol + (size_t)(q0 + 32 * mb) * rs;
+      const int rlast = T - 1 - (q0 + 32 * mb + 4 * hi);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int qr = 8 * (i >> 2) + (i & 3);
-        if (q0 + 32 * mb + 4 * hi + qr < T)
-          unsafeAtomicAdd(col + (size_t)qr * rs, acc[i] * p.scale);
+        const int qr = min(8 * (i >> 2) + (i & 3), rlast);
+        unsafeAtomicAdd(col + (size_t)qr * rs, acc[i] * p.scale);
       }
     }
   };
 
+  // Tile loop. Each tile issues NMB*16 dQ atomics after the prefetch of the next tile, and
+  // vector-memory counts retire in issue order, so waiting for vmcnt <= NMB*16 at the top of
+  // the next tile waits for that prefetch without waiting for the atomics.
   load_qtile<D>(p, qbase, obase, l2base, dlbase, Q0, O0, L0, D0, qt_lo, wave, lane);
   wait_vmem();
   __syncthreads();
   for (int qt = qt_lo; qt <= qt_hi; qt += 2) {
     if (qt + 1 <= qt_hi) load_qtile<D>(p, qbase, obase, l2base, dlbase, Q1, O1, L1, D1, qt + 1, wave, lane);
     tile(Q0, O0, L0, D0, qt);
-    wait_vmem();
-    __syncthreads();
     if (qt + 1 > qt_hi) break;
+    wait_vmem_but<NMB * 16>();
+    lds_sync();
     if (qt + 2 <= qt_hi) load_qtile<D>(p, qbase, obase, l2base, dlbase, Q0, O0, L0, D0, qt + 2, wave, lane);
     tile(Q1, O1, L1, D1, qt + 1);
-    wait_vmem();
-    __syncthreads();
+    if (qt + 2 > qt_hi) break;
+    wait_vmem_but<NMB * 16>();
+    lds_sync();
   }
 
   // Epilogue: lane owns d = 32 db + l32 of keys kw + 8(i/4) + 4 hi + (i%4).

@@ -60,6 +60,14 @@ __device__ __forceinline__ void g2lds16(const void* gsrc, lds_t<bf16>* lds_base)
 // Wait until this wave's outstanding vector-memory operations (incl. LDS DMA) have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
+// Wait until at most N vector-memory operations of this wave are outstanding (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmem_but() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
 // Transposing LDS read: each 16-lane group reads a 4 x 16 block of b16 (lane j gives the
 // address of row j/4, columns 4(j%4)..+3) and lane i receives column i, rows 0..3.
 __device__ __forceinline__ bf16x4 ds_read_tr16(const lds_t<bf16>* p) {
@@ -84,6 +92,26 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 // be speculated, so the compiler keeps the branch instead of executing the body unconditionally
 // under a select.
 __device__ __forceinline__ void branch_keep() { asm volatile("" ::: "memory"); }
+
+// Workgroup barrier for LDS data produced by ds_* stores only: waits for this wave's LDS
+// operations (lgkmcnt(0)) but not for outstanding global loads, async global->LDS copies or
+// atomics, then s_barrier; empty volatile asm on both sides keeps the compiler from moving
+// memory accesses across it. (__syncthreads() also drains vmcnt, which would expose the latency
+// of in-flight prefetches and atomics.) Data written by async copies needs wait_vmem* first.
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt/expcnt left at their maxima
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// 8-byte LDS store issued as a plain ds_write_b64. The compiler conservatively drains all
+// outstanding vector-memory operations before a normal LDS store while async global->LDS
+// copies are in flight; the stores that use this helper go to an LDS array those copies never
+// write, and lds_sync() waits for them (lgkmcnt(0)) before any other wave reads them.
+__device__ __forceinline__ void ds_store_b64(lds_t<bf16>* p, unsigned long long v) {
+  asm volatile("ds_write_b64 %0, %1" : : "v"((unsigned)(size_t)p), "v"(v) : "memory");
+}
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
