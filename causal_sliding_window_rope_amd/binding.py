@@ -37,9 +37,9 @@ SIGNATURES = {
     "swa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
                      _I, _I, _I, _I, _I, _F, _I, _P]),
     "swa_bwd_preprocess": (_I, [_P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _P]),
-    "swa_bwd_main": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
+    "swa_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
                           _I, _I, _I, _I, _I, _F, _I, _P]),
-    "swa_bwd_finalize": (_I, [_P, _P, _S, _I, _I, _I, _I, _I, _P]),
+    "swa_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _F, _I, _P]),
 }
 
 _lib = None
@@ -207,9 +207,8 @@ def swa_bwd(q, k, v, o, lse, dO, window: int, scale: float | None = None, ve=Non
 
 
 def swa_bwd_stages(q, k, v, o, lse, dO, window: int, scale: float | None = None, ve=None,
-                   gate=None, workspace=None, grads=None, events=None):
-    """swa_bwd as its three C-ABI stages. ``events`` = (start, end) torch.cuda.Event pair
-    recorded around swa_bwd_main on the current stream (for timing the main kernel)."""
+                   gate=None, workspace=None, grads=None):
+    """swa_bwd as its three C-ABI stages: preprocess, dK/dV, dQ."""
     B, T, H, D = q.shape
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     ws_bytes = swa_bwd_workspace_size(B, T, H, D, q.dtype)
@@ -223,16 +222,14 @@ def swa_bwd_stages(q, k, v, o, lse, dO, window: int, scale: float | None = None,
     else:
         dq, dk, dv, dve, dgate = grads
     st = _stream()
-    _call("swa_bwd_preprocess", _ptr(o), _ptr(dO), _ptr(lse), _ptr(workspace), nbytes, B, T, H, D, _dt(q),
+    dt = _dt(q)
+    _call("swa_bwd_preprocess", _ptr(o), _ptr(dO), _ptr(lse), _ptr(workspace), nbytes, B, T, H, D, dt,
           st)
-    if events is not None:
-        events[0].record()
-    _call("swa_bwd_main", _ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), _ptr(lse), _ptr(dO),
-          _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dve), _ptr(dgate), _ptr(workspace), nbytes, B, T, H, D,
-          int(window), float(scale), _dt(q), st)
-    if events is not None:
-        events[1].record()
-    _call("swa_bwd_finalize", _ptr(dq), _ptr(workspace), nbytes, B, T, H, D, _dt(q), st)
+    _call("swa_bwd_dkdv", _ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), _ptr(lse), _ptr(dO),
+          _ptr(dk), _ptr(dv), _ptr(dve), _ptr(dgate), _ptr(workspace), nbytes, B, T, H, D,
+          int(window), float(scale), dt, st)
+    _call("swa_bwd_dq", _ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), _ptr(lse), _ptr(dO),
+          _ptr(dq), _ptr(workspace), nbytes, B, T, H, D, int(window), float(scale), dt, st)
     if ve is not None:
         return dq, dk, dv, dve, dgate
     return dq, dk, dv

@@ -215,8 +215,8 @@ int swa_bwd(const void* q, const void* k, const void* v, const void* ve, const f
   const hipStream_t s = (hipStream_t)stream;
   hipError_t e = swa::launch_bwd_pre(a, o, dO, lse, workspace, bf, s);
   if (e == hipSuccess)
-    e = swa::launch_bwd_main(a, q, k, v, ve, gate, lse, dO, dq, dk, dv, dve, dgate, workspace, bf, s);
-  if (e == hipSuccess) e = swa::launch_bwd_final(a, dq, workspace, bf, s);
+    e = swa::launch_bwd_dkdv(a, q, k, v, ve, gate, lse, dO, dk, dv, dve, dgate, workspace, bf, s);
+  if (e == hipSuccess) e = swa::launch_bwd_dq(a, q, k, v, ve, gate, lse, dO, dq, workspace, bf, s);
   return hip_status(e, fn);
 }
 
@@ -230,26 +230,34 @@ int swa_bwd_preprocess(const void* o, const void* dO, const float* lse, void* wo
   return hip_status(swa::launch_bwd_pre(a, o, dO, lse, workspace, dtype == SWA_BF16, (hipStream_t)stream), fn);
 }
 
-int swa_bwd_main(const void* q, const void* k, const void* v, const void* ve, const float* gate,
-                 const float* lse, const void* dO, void* dq, void* dk, void* dv, void* dve,
-                 float* dgate, void* workspace, size_t ws_bytes, int B, int T, int H, int D,
-                 int window, float scale, swa_dtype dtype, void* stream) {
-  const char* fn = "swa_bwd_main";
+int swa_bwd_dkdv(const void* q, const void* k, const void* v, const void* ve, const float* gate,
+                 const float* lse, const void* dO, void* dk, void* dv, void* dve, float* dgate,
+                 void* workspace, size_t ws_bytes, int B, int T, int H, int D, int window,
+                 float scale, swa_dtype dtype, void* stream) {
+  const char* fn = "swa_bwd_dkdv";
   swa::AttnShape a;
-  SWA_TRY(check_bwd(fn, q, k, v, ve, gate, nullptr, lse, dO, dq, dk, dv, dve, dgate, workspace,
+  // dq is not used by this stage; dk stands in for it in the shared checks
+  SWA_TRY(check_bwd(fn, q, k, v, ve, gate, nullptr, lse, dO, dk, dk, dv, dve, dgate, workspace,
                     ws_bytes, B, T, H, D, window, scale, dtype, &a));
-  return hip_status(swa::launch_bwd_main(a, q, k, v, ve, gate, lse, dO, dq, dk, dv, dve, dgate,
+  return hip_status(swa::launch_bwd_dkdv(a, q, k, v, ve, gate, lse, dO, dk, dv, dve, dgate,
                                          workspace, dtype == SWA_BF16, (hipStream_t)stream), fn);
 }
 
-int swa_bwd_finalize(void* dq, void* workspace, size_t ws_bytes, int B, int T, int H, int D,
-                     swa_dtype dtype, void* stream) {
-  const char* fn = "swa_bwd_finalize";
+int swa_bwd_dq(const void* q, const void* k, const void* v, const void* ve, const float* gate,
+               const float* lse, const void* dO, void* dq, void* workspace, size_t ws_bytes, int B,
+               int T, int H, int D, int window, float scale, swa_dtype dtype, void* stream) {
+  const char* fn = "swa_bwd_dq";
   SWA_TRY(check_shape(fn, B, T, H, D, dtype));
-  SWA_TRY(need(fn, "dq", dq));
+  SWA_TRY(need(fn, "q", q)); SWA_TRY(need(fn, "k", k)); SWA_TRY(need(fn, "v", v));
+  SWA_TRY(need(fn, "lse", lse)); SWA_TRY(need(fn, "dO", dO)); SWA_TRY(need(fn, "dq", dq));
+  if ((ve != nullptr) != (gate != nullptr))
+    return fail(SWA_ERR_INVALID_ARG, "%s: ve and gate must be given together", fn);
+  SWA_TRY(opt(fn, "ve", ve));
+  swa::AttnShape a{B, T, H, D, 0, scale};
+  SWA_TRY(check_window_scale(fn, window, scale, T, &a.window));
   SWA_TRY(check_ws(fn, workspace, ws_bytes, B, T, H, D, dtype));
-  swa::AttnShape a{B, T, H, D, T, 1.f};
-  return hip_status(swa::launch_bwd_final(a, dq, workspace, dtype == SWA_BF16, (hipStream_t)stream), fn);
+  return hip_status(swa::launch_bwd_dq(a, q, k, v, ve, gate, lse, dO, dq, workspace,
+                                       dtype == SWA_BF16, (hipStream_t)stream), fn);
 }
 
 }  // extern "C"

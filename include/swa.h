@@ -139,15 +139,14 @@ int swa_fwd(const void* q, const void* k, const void* v, const void* ve, const f
             void* o, float* lse, int B, int T, int H, int D, int window, float scale,
             swa_dtype dtype, void* stream);
 
-/* Bytes of workspace swa_bwd needs: the row terms delta and lse*log2(e) (each (B,H,T) float32)
- * and, for bf16, a float32 dq accumulator (B,T,H,D); each 256-byte aligned inside the block,
- * the row-term arrays followed by 512 bytes of slack. */
+/* Bytes of workspace swa_bwd needs: the row terms delta and lse*log2(e), each (B,H,T) float32,
+ * 256-byte aligned inside the block and followed by 512 bytes of slack. */
 size_t swa_bwd_workspace_size(int B, int T, int H, int D, swa_dtype dtype);
 
 /*
  * swa_bwd — backward of swa_fwd with score recomputation ("GPT-2 124M 复现" §19).
  *   P = exp(s - lse); dv_eff = P^T dO; dP = dO v_eff^T; delta_i = dO_i . O_i;
- *   dS = P * (dP - delta); dq = scale dS k; dk = scale dS^T q.
+ *   dS = P * (dP - delta); dq = scale dS k; dk = scale dS^T q. Outputs are bitwise repeatable.
  *   With the gate: dv = dv_eff, dve = gate * dv_eff, dgate = sum_d dv_eff * ve.
  *   q, k, v, ve, gate: as given to swa_fwd.  o, lse: swa_fwd's outputs.  dO: (B,T,H,D) dtype.
  *   dq, dk, dv: device (B,T,H,D) dtype, written.
@@ -164,27 +163,29 @@ int swa_bwd(const void* q, const void* k, const void* v, const void* ve, const f
  * The three stages swa_bwd runs, for callers that schedule or time them separately. Call them
  * in this order on one stream with one workspace (same sizes and dtype throughout):
  *
- * swa_bwd_preprocess — delta_i = dO_i . O_i and lse_i * log2(e) into the workspace; for SWA_BF16
- *   also zeroes the float32 dq accumulator in the workspace.
+ * swa_bwd_preprocess — delta_i = dO_i . O_i and lse_i * log2(e) into the workspace.
  */
 int swa_bwd_preprocess(const void* o, const void* dO, const float* lse, void* workspace,
                        size_t ws_bytes, int B, int T, int H, int D, swa_dtype dtype, void* stream);
 
 /*
- * swa_bwd_main — the recomputing backward proper (arguments as swa_bwd, without o). Writes dk,
- *   dv (dve, dgate); writes dq for SWA_F32; for SWA_BF16 adds scale * dS k into the workspace's
- *   dq accumulator (dq itself is written by swa_bwd_finalize).
+ * swa_bwd_dkdv — the key-block-major part of the recomputing backward (arguments as swa_bwd,
+ *   without o and dq): writes dk, dv (and dve, dgate with the gate). Needs the workspace
+ *   filled by swa_bwd_preprocess.
  */
-int swa_bwd_main(const void* q, const void* k, const void* v, const void* ve, const float* gate,
-                 const float* lse, const void* dO, void* dq, void* dk, void* dv, void* dve,
-                 float* dgate, void* workspace, size_t ws_bytes, int B, int T, int H, int D,
-                 int window, float scale, swa_dtype dtype, void* stream);
+int swa_bwd_dkdv(const void* q, const void* k, const void* v, const void* ve, const float* gate,
+                 const float* lse, const void* dO, void* dk, void* dv, void* dve, float* dgate,
+                 void* workspace, size_t ws_bytes, int B, int T, int H, int D, int window,
+                 float scale, swa_dtype dtype, void* stream);
 
 /*
- * swa_bwd_finalize — SWA_BF16: dq = bf16(dq accumulator). SWA_F32: validates and does nothing.
+ * swa_bwd_dq — the query-block-major part: recomputes the scores per query block and writes
+ *   dq = scale * dS k directly (no atomics; bitwise repeatable). Needs the workspace filled by
+ *   swa_bwd_preprocess. May run before, after or concurrently with swa_bwd_dkdv.
  */
-int swa_bwd_finalize(void* dq, void* workspace, size_t ws_bytes, int B, int T, int H, int D,
-                     swa_dtype dtype, void* stream);
+int swa_bwd_dq(const void* q, const void* k, const void* v, const void* ve, const float* gate,
+               const float* lse, const void* dO, void* dq, void* workspace, size_t ws_bytes, int B,
+               int T, int H, int D, int window, float scale, swa_dtype dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -75,7 +75,7 @@ def test_swa_fwd_validation(lib):
 
 def test_swa_bwd_validation(lib):
     ws_need = lib.swa_bwd_workspace_size(2, 64, 3, 64, 1)
-    assert ws_need >= 2 * 64 * 3 * 4 + 2 * 64 * 3 * 64 * 4
+    assert ws_need >= 2 * (2 * 64 * 3 * 4)          # delta and lse*log2(e), float32 each
     assert lib.swa_bwd_workspace_size(2, 64, 3, 96, 1) == 0
 
     def bwd(ws=P, ws_bytes=ws_need, ve=None, gate=None, dve=None, dgate=None, W=8, dO=P):
@@ -89,6 +89,20 @@ def test_swa_bwd_validation(lib):
     assert bwd(dve=P, dgate=P) == INVALID               # dve/dgate without gate
     assert bwd(W=0) == INVALID
     assert bwd(dO=None) == INVALID
+
+    # the two compute stages check the same arguments
+    def dkdv(ws=P, ws_bytes=ws_need, W=8):
+        return lib.swa_bwd_dkdv(P, P, P, None, None, P, P, P, P, None, None, ws, ws_bytes, 2, 64, 3,
+                                64, W, 0.125, 1, None)
+
+    def dq(ws=P, ws_bytes=ws_need, W=8, ve=None, gate=None):
+        return lib.swa_bwd_dq(P, P, P, ve, gate, P, P, P, ws, ws_bytes, 2, 64, 3, 64, W, 0.125, 1,
+                              None)
+
+    assert dkdv(ws=None) == WORKSPACE and dq(ws=None) == WORKSPACE
+    assert dkdv(ws_bytes=ws_need - 1) == WORKSPACE and dq(ws_bytes=ws_need - 1) == WORKSPACE
+    assert dkdv(W=0) == INVALID and dq(W=0) == INVALID
+    assert dq(ve=P) == INVALID                          # ve without gate
 
 
 def test_prologue_and_gate_validation(lib):
