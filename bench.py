@@ -221,25 +221,38 @@ def run_bench(args):
     return result
 
 
+# source files each timed kernel is compiled from (a change to any of them invalidates the
+# committed counter figures for that kernel)
+KERNEL_SOURCES = {
+    "fwd_bf16_kernel": ("fwd.hip", "common.h"),
+    "dkdv_bf16_kernel": ("bwd.hip", "common.h"),
+    "dq_bf16_kernel": ("dq.hip", "common.h"),
+}
+
+
+def kernel_sources_sha256(kernel: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "causal_sliding_window_rope_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def traffic_from_profile(kernel: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
-    current kernel source (its sha256 is recorded there); otherwise None."""
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by its copy-kernel calibration factor), if the
+    counters were taken on the current kernel sources; otherwise None."""
     path = os.path.join(ROOT, "profiles", "counters.json")
-    if not os.path.exists(path):
+    name = kernel.split()[0]
+    if name not in KERNEL_SOURCES or not os.path.exists(path):
         return None
     try:
         with open(path) as f:
-            prof = json.load(f)
-    except (OSError, ValueError):
+            ent = json.load(f)[workload]["kernels"][name]
+    except (OSError, ValueError, KeyError):
         return None
-    key = "bwd" if kernel.startswith("bwd") else "fwd"
-    ent = prof.get(workload, {}).get(key)
-    if not ent:
+    if ent.get("sources_sha256") != kernel_sources_sha256(name):
         return None
-    src = os.path.join(ROOT, "causal_sliding_window_rope_amd", "csrc", ent["source"])
-    with open(src, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != ent["source_sha256"]:
-            return None
     return ent["hbm_bytes_per_launch"]
 
 
