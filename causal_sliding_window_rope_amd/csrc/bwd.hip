@@ -116,7 +116,7 @@ __device__ __forceinline__ void load_qtile(const Params& p, const bf16* qbase, c
 }
 
 template <int D, bool GATE>
-__global__ void __launch_bounds__(256, 1) dkdv_bf16_kernel(Params p) {
+__global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dkdv_bf16_kernel(Params p) {
   using C = Cfg<D>;
   constexpr int NDB = D / 32, NKS = D / 16;
   __shared__ __attribute__((aligned(16))) bf16 q0_[C::QTILE], q1_[C::QTILE], o0_[C::QTILE],
@@ -212,24 +212,50 @@ __global__ void __launch_bounds__(256, 1) dkdv_bf16_kernel(Params p) {
       if (skip) continue;
       const bool need_mask = (qm < kw + 31) || (qm + 31 > kw + W - 1) || (qm + 32 > T) ||
                              (kw + 32 > T);
-      f32x16 s = (f32x16){}, dp = (f32x16){};
+      // The LDS operands of each phase are requested together, one phase ahead where registers
+      // allow, so the reads overlap one another and the MFMAs of the previous phase; the waits
+      // before the MFMAs then count down instead of draining the LDS queue each time.
+      bf16x8 aq[NKS], ao[NKS];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const int off = mb * 32 * D + rowb[ks];
-        const bf16x8 aq = *reinterpret_cast<const lds_t<bf16x8>*>(Qs + off);
-        const bf16x8 ao = *reinterpret_cast<const lds_t<bf16x8>*>(Os + off);
-        s = mfma32(aq, kreg[ks], s);
-        dp = mfma32(ao, vreg[ks], dp);
+        aq[ks] = *reinterpret_cast<const lds_t<bf16x8>*>(Qs + off);
+        ao[ks] = *reinterpret_cast<const lds_t<bf16x8>*>(Os + off);
       }
+      f32x4 l2v[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        l2v[a] = *reinterpret_cast<const lds_t<f32x4>*>(Ls + mb * 32 + 8 * a + 4 * hi);
+      sched_fence();
+      // S = Q K^T and dP = dO V^T (lane = key, 16 queries per lane)
+      f32x16 s = (f32x16){}, dp = (f32x16){};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        s = mfma32(aq[ks], kreg[ks], s);
+        dp = mfma32(ao[ks], vreg[ks], dp);
+      }
+      // B operands of dV += P^T dO by transposing reads of the row-major dO tile; delta
+      bf16x8 bo[NDB][2];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) {
+          const int ro = (mb * 32 + sp * 16) * D;
+          bo[db][sp] = __builtin_shufflevector(ds_read_tr16(Os + ro + trb1[db]),
+                                               ds_read_tr16(Os + ro + trb2[db]),
+                                               0, 1, 2, 3, 4, 5, 6, 7);
+        }
+      f32x4 dlv[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        dlv[a] = *reinterpret_cast<const lds_t<f32x4>*>(Dls + mb * 32 + 8 * a + 4 * hi);
       sched_fence();
       float pv[16];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const f32x4 l2 = *reinterpret_cast<const lds_t<f32x4>*>(Ls + mb * 32 + 8 * a + 4 * hi);
+      for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          pv[4 * a + r] = __builtin_amdgcn_exp2f(fmaf(s[4 * a + r], p.c, -l2[r]));
-      }
+          pv[4 * a + r] = __builtin_amdgcn_exp2f(fmaf(s[4 * a + r], p.c, -l2v[a][r]));
       if (need_mask) {
         branch_keep();
         // query qm + 8a + 4hi + r is visible to key `mykey` iff (q - mykey) in [0, mask_n)
@@ -240,40 +266,50 @@ __global__ void __launch_bounds__(256, 1) dkdv_bf16_kernel(Params p) {
           pv[i] = ((unsigned)(base + t) < mask_n) ? pv[i] : 0.f;
         }
       }
-      bf16x8 pb[2], sbf[2];
+      bf16x8 pb[2];
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const f32x4 dl = *reinterpret_cast<const lds_t<f32x4>*>(Dls + mb * 32 + 8 * a + 4 * hi);
-        float dsv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dsv[r] = pv[4 * a + r] * (dp[4 * a + r] - dl[r]);
         const bf16x2 p01 = __builtin_convertvector((f32x2){pv[4 * a], pv[4 * a + 1]}, bf16x2);
         const bf16x2 p23 = __builtin_convertvector((f32x2){pv[4 * a + 2], pv[4 * a + 3]}, bf16x2);
-        const bf16x2 d01 = __builtin_convertvector((f32x2){dsv[0], dsv[1]}, bf16x2);
-        const bf16x2 d23 = __builtin_convertvector((f32x2){dsv[2], dsv[3]}, bf16x2);
         const int e0 = 4 * (a & 1);
         pb[a >> 1][e0] = p01[0]; pb[a >> 1][e0 + 1] = p01[1];
         pb[a >> 1][e0 + 2] = p23[0]; pb[a >> 1][e0 + 3] = p23[1];
-        sbf[a >> 1][e0] = d01[0]; sbf[a >> 1][e0 + 1] = d01[1];
-        sbf[a >> 1][e0 + 2] = d23[0]; sbf[a >> 1][e0 + 3] = d23[1];
       }
-      // dV += P^T dO and dK += dS^T Q; B operands by transposing reads of the row-major tiles.
+      sched_fence();
+      // dV += P^T dO, with the Q^T reads for dK and the dS arithmetic issued alongside
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) dv[db] = mfma32(pb[sp], bo[db][sp], dv[db]);
+      bf16x8 bq[NDB][2];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int sp = 0; sp < 2; ++sp) {
           const int ro = (mb * 32 + sp * 16) * D;
-          const bf16x8 bo = __builtin_shufflevector(ds_read_tr16(Os + ro + trb1[db]),
-                                                    ds_read_tr16(Os + ro + trb2[db]),
-                                                    0, 1, 2, 3, 4, 5, 6, 7);
-          const bf16x8 bq = __builtin_shufflevector(ds_read_tr16(Qs + ro + trb1[db]),
-                                                    ds_read_tr16(Qs + ro + trb2[db]),
-                                                    0, 1, 2, 3, 4, 5, 6, 7);
-          dv[db] = mfma32(pb[sp], bo, dv[db]);
-          dk[db] = mfma32(sbf[sp], bq, dk[db]);
+          bq[db][sp] = __builtin_shufflevector(ds_read_tr16(Qs + ro + trb1[db]),
+                                               ds_read_tr16(Qs + ro + trb2[db]),
+                                               0, 1, 2, 3, 4, 5, 6, 7);
         }
-        sched_fence();
+      bf16x8 sbf[2];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        float dsv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dsv[r] = pv[4 * a + r] * (dp[4 * a + r] - dlv[a][r]);
+        const bf16x2 d01 = __builtin_convertvector((f32x2){dsv[0], dsv[1]}, bf16x2);
+        const bf16x2 d23 = __builtin_convertvector((f32x2){dsv[2], dsv[3]}, bf16x2);
+        const int e0 = 4 * (a & 1);
+        sbf[a >> 1][e0] = d01[0]; sbf[a >> 1][e0 + 1] = d01[1];
+        sbf[a >> 1][e0 + 2] = d23[0]; sbf[a >> 1][e0 + 3] = d23[1];
       }
+      sched_fence();
+      // dK += dS^T Q
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) dk[db] = mfma32(sbf[sp], bq[db][sp], dk[db]);
+      sched_fence();
     }
   };
 

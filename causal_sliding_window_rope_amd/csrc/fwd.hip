@@ -124,26 +124,47 @@ struct WaveState {
 // One 64-key tile for one wave (32 query rows): S^T = K Q^T, mask, online softmax, O^T += V^T P^T.
 template <int D>
 __device__ __forceinline__ void tile_step(WaveState<D>& ws, const bf16x8* qreg,
-                                          const lds_t<bf16>* ks, const lds_t<bf16>* vs, int k0,
-                                          int qw, int myq, int T, int W, float c, int lane) {
+                                          const lds_t<bf16>* ks, const lds_t<bf16>* vs,
+                                          const int* krow, const int* vtr1, const int* vtr2,
+                                          int k0, int qw, int myq, int T, int W, float c,
+                                          int lane) {
   constexpr int NKS = D / 16, NDB = D / 32;
   const int l32 = lane & 31, hi = lane >> 5;
   const bool skip = (k0 > qw + 31) || (k0 + BN - 1 < qw - W + 1);
   if (skip) return;
   const bool need_mask = (k0 + BN - 1 > qw) || (k0 < qw + 31 - W + 1) || (k0 + BN > T);
+  // All K operands of the tile are requested before the S MFMAs and all V^T operands right
+  // after them, so the LDS reads overlap one another (and the softmax arithmetic) instead of
+  // each MFMA waiting for its own read.
+  bf16x8 ka0[NKS], ka1[NKS];
+#pragma unroll
+  for (int kk = 0; kk < NKS; ++kk) ka0[kk] = *reinterpret_cast<const lds_t<bf16x8>*>(ks + krow[kk]);
+  sched_fence();
   f32x16 s[2];
+  s[0] = (f32x16){};
+  s[1] = (f32x16){};
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    s[kb] = (f32x16){};
-    const int m = kb * 32 + l32;
-    const lds_t<bf16>* arow = ks + m * D;
-    const int sw = swz<D>(m);
+  for (int kk = 0; kk < NKS; ++kk) s[0] = mfma32(ka0[kk], qreg[kk], s[0]);
 #pragma unroll
-    for (int kk = 0; kk < NKS; ++kk) {
-      const bf16x8 a = *reinterpret_cast<const lds_t<bf16x8>*>(arow + 8 * ((2 * kk + hi) ^ sw));
-      s[kb] = mfma32(a, qreg[kk], s[kb]);
-    }
-  }
+  for (int kk = 0; kk < NKS; ++kk)
+    ka1[kk] = *reinterpret_cast<const lds_t<bf16x8>*>(ks + 32 * D + krow[kk]);
+  sched_fence();
+#pragma unroll
+  for (int kk = 0; kk < NKS; ++kk) s[1] = mfma32(ka1[kk], qreg[kk], s[1]);
+  auto read_v = [&](bf16x8 (&dst)[NDB][2], int kb) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int sp = 0; sp < 2; ++sp) {
+        const int ro = (kb * 32 + sp * 16) * D;
+        dst[db][sp] = __builtin_shufflevector(ds_read_tr16(vs + ro + vtr1[db]),
+                                              ds_read_tr16(vs + ro + vtr2[db]),
+                                              0, 1, 2, 3, 4, 5, 6, 7);
+      }
+  };
+  bf16x8 va0[NDB][2];
+  read_v(va0, 0);
+  sched_fence();
   if (need_mask) {
     branch_keep();
     // key k0 + t is visible iff t - lo lies in [0, n): lo, n from the row's window and T
@@ -197,23 +218,18 @@ __device__ __forceinline__ void tile_step(WaveState<D>& ws, const bf16x8* qreg,
       }
     }
   ws.l_run += lsum;
-  // O^T += V^T P^T; the V^T operand comes from the row-major V tile by transposing reads.
-  const int g = lane >> 4, j = lane & 15;
+  sched_fence();
+  // O^T += V^T P^T
+  bf16x8 va1[NDB][2];
+  read_v(va1, 1);
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    const int d = 32 * db + 16 * (g & 1) + 4 * (j & 3);
-    const int cc = d >> 3, half = (d >> 2) & 1;
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int sp = 0; sp < 2; ++sp) ws.oacc[db] = mfma32(va0[db][sp], pb[0][sp], ws.oacc[db]);
 #pragma unroll
-      for (int sp = 0; sp < 2; ++sp) {
-        const int r1 = kb * 32 + sp * 16 + 4 * hi + (j >> 2), r2 = r1 + 8;
-        const bf16x4 lo = ds_read_tr16(vs + r1 * D + 8 * (cc ^ swz<D>(r1)) + 4 * half);
-        const bf16x4 up = ds_read_tr16(vs + r2 * D + 8 * (cc ^ swz<D>(r2)) + 4 * half);
-        const bf16x8 a = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
-        ws.oacc[db] = mfma32(a, pb[kb][sp], ws.oacc[db]);
-      }
-  }
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp) ws.oacc[db] = mfma32(va1[db][sp], pb[1][sp], ws.oacc[db]);
 }
 
 template <int D, bool GATE>
@@ -267,6 +283,24 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(Params p) {
   ws.m_ref = -INFINITY;
   ws.l_run = 0.f;
 
+  // Lane-constant LDS element offsets (plus compile-time row offsets at each use): K rows for
+  // the S^T MFMA A operand (row l32, chunk 2 kk + hi) and the two transposing reads of V^T
+  // (rows 4 hi + (j / 4) and + 8, 4 dims of d-block db), all through the chunk swizzle, which
+  // depends only on the row modulo 16.
+  int krow[NKS], vtr1[NDB], vtr2[NDB];
+#pragma unroll
+  for (int kk = 0; kk < NKS; ++kk) krow[kk] = l32 * D + 8 * ((2 * kk + hi) ^ swz<D>(l32));
+  {
+    const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d = 32 * db + 16 * (g & 1) + 4 * (j & 3);
+      const int r1 = 4 * hi + (j >> 2), r2 = r1 + 8;
+      vtr1[db] = r1 * D + 8 * ((d >> 3) ^ swz<D>(r1)) + 4 * ((d >> 2) & 1);
+      vtr2[db] = r2 * D + 8 * ((d >> 3) ^ swz<D>(r2)) + 4 * ((d >> 2) & 1);
+    }
+  }
+
   Tiles<D, GATE> tl;
   tl.init(H, wave, lane);
   tl.load(p, kbase, vbase, K0, V0, kt_lo, tid);
@@ -275,12 +309,12 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(Params p) {
   // Two tiles per trip so that each LDS buffer is named statically.
   for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
     if (kt + 1 <= kt_hi) tl.load(p, kbase, vbase, K1, V1, kt + 1, tid);
-    tile_step<D>(ws, qreg, K0, V0, kt * BN, qw, myq, T, W, p.c, lane);
+    tile_step<D>(ws, qreg, K0, V0, krow, vtr1, vtr2, kt * BN, qw, myq, T, W, p.c, lane);
     wait_vmem();
     __syncthreads();
     if (kt + 1 > kt_hi) break;
     if (kt + 2 <= kt_hi) tl.load(p, kbase, vbase, K0, V0, kt + 2, tid);
-    tile_step<D>(ws, qreg, K1, V1, (kt + 1) * BN, qw, myq, T, W, p.c, lane);
+    tile_step<D>(ws, qreg, K1, V1, krow, vtr1, vtr2, (kt + 1) * BN, qw, myq, T, W, p.c, lane);
     wait_vmem();
     __syncthreads();
   }
