@@ -26,7 +26,7 @@ template <int D> struct Cfg {
   static constexpr int NI = BN / RPI;
   static constexpr int NIW = NI / NW;
   static constexpr int TILE = BN * D;
-  static constexpr int CPT = BN * CH / 256;
+  static constexpr int CPT = BN * CH / (64 * NW);
 };
 
 struct Params {
@@ -76,7 +76,7 @@ struct Tiles {
     } else {
 #pragma unroll
       for (int j = 0; j < C::CPT; ++j) {
-        const int id = tid + 256 * j;
+        const int id = tid + 64 * NW * j;
         const int r = id / C::CH, pos = id % C::CH;
         const int c = pos ^ swz<D>(r);
         const int grow = min(kt * BN + r, p.T - 1);
@@ -159,7 +159,7 @@ __device__ __forceinline__ void dq_tile(f32x16* dqacc, const bf16x8* qreg, const
 }
 
 template <int D, bool GATE>
-__global__ void __launch_bounds__(256, 2) dq_bf16_kernel(Params p) {
+__global__ void __launch_bounds__(64 * NW, 8 / NW) dq_bf16_kernel(Params p) {
   using C = Cfg<D>;
   constexpr int NDB = D / 32, NKS = D / 16;
   __shared__ __attribute__((aligned(16))) bf16 k0s[C::TILE], v0s[C::TILE], k1s[C::TILE], v1s[C::TILE];
@@ -260,7 +260,7 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(Params p) {
 template <int D, bool GATE>
 static hipError_t launch_t(const AttnShape& a, const Params& p, hipStream_t s) {
   const unsigned blocks = (unsigned)p.nqb * a.B * a.H;
-  hipLaunchKernelGGL((dq_bf16_kernel<D, GATE>), dim3(blocks), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((dq_bf16_kernel<D, GATE>), dim3(blocks), dim3(64 * dqk::NW), 0, s, p);
   return hipGetLastError();
 }
 

@@ -38,7 +38,7 @@ template <int D> struct Cfg {
   static constexpr int NI = BN / RPI;       // 1 KiB loads per tile
   static constexpr int NIW = NI / NW;       // ... per wave
   static constexpr int TILE = BN * D;       // elements per K or V tile
-  static constexpr int CPT = BN * CH / 256; // chunks per thread (register-staged gate path)
+  static constexpr int CPT = BN * CH / (64 * NW);   // chunks per thread (register-staged gate path)
 };
 
 struct Params {
@@ -95,7 +95,7 @@ struct Tiles {
       // v_eff = v + gate * ve is formed in fp32 on the way into LDS
 #pragma unroll
       for (int j = 0; j < C::CPT; ++j) {
-        const int id = tid + 256 * j;
+        const int id = tid + 64 * NW * j;
         const int r = id / C::CH, pos = id % C::CH;
         const int c = pos ^ swz<D>(r);
         const int grow = min(kt * BN + r, T - 1);
@@ -233,7 +233,7 @@ __device__ __forceinline__ void tile_step(WaveState<D>& ws, const bf16x8* qreg,
 }
 
 template <int D, bool GATE>
-__global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(Params p) {
+__global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(Params p) {
   using C = Cfg<D>;
   constexpr int NDB = D / 32;
   constexpr int NKS = D / 16;
@@ -394,7 +394,7 @@ static hipError_t launch_fwd_bf16_t(const AttnShape& a, const void* q, const voi
   p.nqb = (a.T + fwdk::BM - 1) / fwdk::BM;
   p.c = a.scale * kLog2e;
   const unsigned blocks = (unsigned)p.nqb * a.B * a.H;
-  hipLaunchKernelGGL((fwdk::fwd_bf16_kernel<D, GATE>), dim3(blocks), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((fwdk::fwd_bf16_kernel<D, GATE>), dim3(blocks), dim3(64 * fwdk::NW), 0, s, p);
   return hipGetLastError();
 }
 
