@@ -27,14 +27,14 @@
 namespace swa {
 
 // ------------------------------------------------------------------------------------------
-// delta_i = sum_d dO[i, d] * O[i, d] and lse2_i = lse_i * log2(e), both (B, H, T).
+// ndelta_i = -sum_d dO[i, d] * O[i, d] and nlse2_i = -lse_i * log2(e), both (B, H, T).
 // ------------------------------------------------------------------------------------------
 template <typename E, int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(const E* __restrict__ o,
                                                       const E* __restrict__ dO,
                                                       const float* __restrict__ lse,
-                                                      float* __restrict__ delta,
-                                                      float* __restrict__ lse2, int rows, int T,
+                                                      float* __restrict__ ndelta,
+                                                      float* __restrict__ nlse2, int rows, int T,
                                                       int H) {
   constexpr int VPT = 16 / sizeof(E), TPR = D / VPT;
   const int lr = threadIdx.x % TPR;
@@ -63,8 +63,9 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const E* __restrict__ o,
   if (lr == 0) {
     const int h = row % H, t = (row / H) % T, b = row / (H * T);
     const size_t r = ((size_t)b * H + h) * T + t;
-    delta[r] = acc;
-    lse2[r] = lse[r] * kLog2e;   // log2-domain row terms for the exp2 in the main kernel
+    // stored negated: the bf16 kernels seed their S and dP accumulators with these
+    ndelta[r] = -acc;
+    nlse2[r] = -lse[r] * kLog2e;   // log2-domain row term of the exp2
   }
 }
 
@@ -83,14 +84,14 @@ template <int D> struct Cfg {
 
 struct Params {
   const bf16* q; const bf16* k; const bf16* v; const bf16* ve; const float* gate;
-  const float* lse2; const float* delta; const bf16* dO;
+  const float* nlse2; const float* ndelta; const bf16* dO;   // row terms, negated
   bf16* dk; bf16* dv; bf16* dve; float* dgate;
   int B, T, H, window, nkb;
   float c;       // scale * log2(e)
   float scale;
 };
 
-// Asynchronous loads of query tile qt (Q, dO rows and the lse2 / delta row terms) into LDS.
+// Asynchronous loads of query tile qt (Q, dO rows and the negated row terms) into LDS.
 template <int D>
 __device__ __forceinline__ void load_qtile(const Params& p, const bf16* qbase, const bf16* obase,
                                            const float* l2base, const float* dlbase,
@@ -149,8 +150,8 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dkdv_bf16_kernel(Params 
   const int mykey = kw + l32;
   const bf16* qbase = p.q + head0;
   const bf16* obase = p.dO + head0;
-  const float* l2base = p.lse2 + (size_t)bh * T;
-  const float* dlbase = p.delta + (size_t)bh * T;
+  const float* l2base = p.nlse2 + (size_t)bh * T;
+  const float* dlbase = p.ndelta + (size_t)bh * T;
 
   // B operands of S = Q K^T and dP = dO V^T: this lane's key row of K and of v_eff.
   bf16x8 kreg[NKS], vreg[NKS];
@@ -171,6 +172,11 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dkdv_bf16_kernel(Params 
         vv.z = pack_bf2(fmaf(gk, bf_lo(ee.z), bf_lo(vv.z)), fmaf(gk, bf_hi(ee.z), bf_hi(vv.z)));
         vv.w = pack_bf2(fmaf(gk, bf_lo(ee.w), bf_lo(vv.w)), fmaf(gk, bf_hi(ee.w), bf_hi(vv.w)));
       }
+      // K pre-scaled by scale * log2(e), so S comes out of the MFMA in exp2 units
+      kk.x = pack_bf2(p.c * bf_lo(kk.x), p.c * bf_hi(kk.x));
+      kk.y = pack_bf2(p.c * bf_lo(kk.y), p.c * bf_hi(kk.y));
+      kk.z = pack_bf2(p.c * bf_lo(kk.z), p.c * bf_hi(kk.z));
+      kk.w = pack_bf2(p.c * bf_lo(kk.w), p.c * bf_hi(kk.w));
       if (!ok) { kk = make_uint4(0, 0, 0, 0); vv = make_uint4(0, 0, 0, 0); }
       kreg[ks] = __builtin_bit_cast(bf16x8, kk);
       vreg[ks] = __builtin_bit_cast(bf16x8, vv);
@@ -222,19 +228,27 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dkdv_bf16_kernel(Params 
         aq[ks] = *reinterpret_cast<const lds_t<bf16x8>*>(Qs + off);
         ao[ks] = *reinterpret_cast<const lds_t<bf16x8>*>(Os + off);
       }
-      f32x4 l2v[4];
+      f32x4 l2v[4], dlv[4];
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < 4; ++a) {
         l2v[a] = *reinterpret_cast<const lds_t<f32x4>*>(Ls + mb * 32 + 8 * a + 4 * hi);
+        dlv[a] = *reinterpret_cast<const lds_t<f32x4>*>(Dls + mb * 32 + 8 * a + 4 * hi);
+      }
       sched_fence();
-      // S = Q K^T and dP = dO V^T (lane = key, 16 queries per lane)
-      f32x16 s = (f32x16){}, dp = (f32x16){};
+      // S' = -lse2 + c Q K^T and dP' = -delta + dO V^T (lane = key, 16 queries per lane): the
+      // accumulators start from the negated row terms of their 16 queries
+      f32x16 s = __builtin_shufflevector(__builtin_shufflevector(l2v[0], l2v[1], 0, 1, 2, 3, 4, 5, 6, 7),
+                                         __builtin_shufflevector(l2v[2], l2v[3], 0, 1, 2, 3, 4, 5, 6, 7),
+                                         0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+      f32x16 dp = __builtin_shufflevector(__builtin_shufflevector(dlv[0], dlv[1], 0, 1, 2, 3, 4, 5, 6, 7),
+                                          __builtin_shufflevector(dlv[2], dlv[3], 0, 1, 2, 3, 4, 5, 6, 7),
+                                          0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         s = mfma32(aq[ks], kreg[ks], s);
         dp = mfma32(ao[ks], vreg[ks], dp);
       }
-      // B operands of dV += P^T dO by transposing reads of the row-major dO tile; delta
+      // B operands of dV += P^T dO by transposing reads of the row-major dO tile
       bf16x8 bo[NDB][2];
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
@@ -245,17 +259,13 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dkdv_bf16_kernel(Params 
                                                ds_read_tr16(Os + ro + trb2[db]),
                                                0, 1, 2, 3, 4, 5, 6, 7);
         }
-      f32x4 dlv[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-        dlv[a] = *reinterpret_cast<const lds_t<f32x4>*>(Dls + mb * 32 + 8 * a + 4 * hi);
       sched_fence();
       float pv[16];
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          pv[4 * a + r] = __builtin_amdgcn_exp2f(fmaf(s[4 * a + r], p.c, -l2v[a][r]));
+          pv[4 * a + r] = __builtin_amdgcn_exp2f(s[4 * a + r]);
       if (need_mask) {
         branch_keep();
         // query qm + 8a + 4hi + r is visible to key `mykey` iff (q - mykey) in [0, mask_n)
@@ -296,7 +306,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dkdv_bf16_kernel(Params 
       for (int a = 0; a < 4; ++a) {
         float dsv[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dsv[r] = pv[4 * a + r] * (dp[4 * a + r] - dlv[a][r]);
+        for (int r = 0; r < 4; ++r) dsv[r] = pv[4 * a + r] * dp[4 * a + r];
         const bf16x2 d01 = __builtin_convertvector((f32x2){dsv[0], dsv[1]}, bf16x2);
         const bf16x2 d23 = __builtin_convertvector((f32x2){dsv[2], dsv[3]}, bf16x2);
         const int e0 = 4 * (a & 1);
@@ -375,7 +385,7 @@ template <int D>
 __global__ void __launch_bounds__(64) bwd_dkdv_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ ve, const float* __restrict__ gate, const float* __restrict__ lse,
-    const float* __restrict__ delta, const float* __restrict__ dO, float* __restrict__ dk,
+    const float* __restrict__ ndelta, const float* __restrict__ dO, float* __restrict__ dk,
     float* __restrict__ dv, float* __restrict__ dve, float* __restrict__ dgate, int T, int H,
     int W, float scale) {
   constexpr int PER = D / 64;
@@ -395,7 +405,7 @@ __global__ void __launch_bounds__(64) bwd_dkdv_f32_kernel(
     const float s = wave_dot<D>(kv, q + qrow * D, lane) * scale;
     const float pij = expf(s - lse[(size_t)bh * T + i]);
     const float dp = wave_dot<D>(vv, dO + qrow * D, lane);
-    const float ds = pij * (dp - delta[(size_t)bh * T + i]);
+    const float ds = pij * (dp + ndelta[(size_t)bh * T + i]);
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
       av[e] = fmaf(pij, dO[qrow * D + lane + 64 * e], av[e]);
@@ -423,7 +433,7 @@ template <int D>
 __global__ void __launch_bounds__(64) bwd_dq_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ ve, const float* __restrict__ gate, const float* __restrict__ lse,
-    const float* __restrict__ delta, const float* __restrict__ dO, float* __restrict__ dq, int T,
+    const float* __restrict__ ndelta, const float* __restrict__ dO, float* __restrict__ dq, int T,
     int H, int W, float scale) {
   constexpr int PER = D / 64;
   const int i = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, lane = threadIdx.x;
@@ -435,7 +445,7 @@ __global__ void __launch_bounds__(64) bwd_dq_f32_kernel(
     ov[e] = dO[qrow * D + lane + 64 * e];
     aq[e] = 0.f;
   }
-  const float L = lse[(size_t)bh * T + i], dl = delta[(size_t)bh * T + i];
+  const float L = lse[(size_t)bh * T + i], ndl = ndelta[(size_t)bh * T + i];
   for (int j = max(0, i - W + 1); j <= i; ++j) {
     const size_t krow = ((size_t)b * T + j) * H + h;
     const float s = wave_dot<D>(qv, k + krow * D, lane) * scale;
@@ -450,7 +460,7 @@ __global__ void __launch_bounds__(64) bwd_dq_f32_kernel(
     }
 #pragma unroll
     for (int m = 32; m > 0; m >>= 1) dp += xor_shfl(dp, m);
-    const float ds = pij * (dp - dl);
+    const float ds = pij * (dp + ndl);
 #pragma unroll
     for (int e = 0; e < PER; ++e) aq[e] = fmaf(ds, k[krow * D + lane + 64 * e], aq[e]);
   }
@@ -460,7 +470,7 @@ __global__ void __launch_bounds__(64) bwd_dq_f32_kernel(
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace: delta (B,H,T) | lse2 (B,H,T), float32. Each block is 256-byte aligned and followed
+// Workspace: -delta (B,H,T) | -lse*log2(e) (B,H,T), float32. Each block is 256-byte aligned and followed
 // by 512 bytes of slack, so the 16-byte row-term loads of a query tile that runs past the
 // sequence end stay inside the allocation.
 static size_t rowterm_block(int B, int T, int H) {
@@ -474,13 +484,13 @@ size_t bwd_workspace_bytes(int B, int T, int H, int D, bool bf16) {
 }
 
 template <typename E, int D>
-static void launch_pre(const void* o, const void* dO, const float* lse, float* delta, float* lse2,
+static void launch_pre(const void* o, const void* dO, const float* lse, float* ndelta, float* nlse2,
                        int B, int T, int H, hipStream_t s) {
   constexpr int TPR = D / (16 / sizeof(E));
   const int rows = B * T * H;
   const int rpb = 256 / TPR;
   hipLaunchKernelGGL((bwd_pre_kernel<E, D>), dim3((rows + rpb - 1) / rpb), dim3(256), 0, s,
-                     (const E*)o, (const E*)dO, lse, delta, lse2, rows, T, H);
+                     (const E*)o, (const E*)dO, lse, ndelta, nlse2, rows, T, H);
 }
 
 template <int D, bool GATE>
@@ -492,14 +502,14 @@ static hipError_t launch_dkdv_bf16_t(const AttnShape& a, const bwdk::Params& p, 
 
 namespace {
 struct WsView {
-  float* delta;
-  float* lse2;
+  float* ndelta;
+  float* nlse2;
 };
 WsView ws_view(void* ws, int B, int T, int H) {
   WsView w;
   char* base = reinterpret_cast<char*>(ws);
-  w.delta = reinterpret_cast<float*>(base);
-  w.lse2 = reinterpret_cast<float*>(base + rowterm_block(B, T, H));
+  w.ndelta = reinterpret_cast<float*>(base);
+  w.nlse2 = reinterpret_cast<float*>(base + rowterm_block(B, T, H));
   return w;
 }
 }  // namespace
@@ -508,11 +518,11 @@ hipError_t launch_bwd_pre(const AttnShape& a, const void* o, const void* dO, con
                           void* ws, bool is_bf16, hipStream_t s) {
   const WsView w = ws_view(ws, a.B, a.T, a.H);
   if (is_bf16) {
-    if (a.D == 64) launch_pre<swa::bf16, 64>(o, dO, lse, w.delta, w.lse2, a.B, a.T, a.H, s);
-    else launch_pre<swa::bf16, 128>(o, dO, lse, w.delta, w.lse2, a.B, a.T, a.H, s);
+    if (a.D == 64) launch_pre<swa::bf16, 64>(o, dO, lse, w.ndelta, w.nlse2, a.B, a.T, a.H, s);
+    else launch_pre<swa::bf16, 128>(o, dO, lse, w.ndelta, w.nlse2, a.B, a.T, a.H, s);
   } else {
-    if (a.D == 64) launch_pre<float, 64>(o, dO, lse, w.delta, w.lse2, a.B, a.T, a.H, s);
-    else launch_pre<float, 128>(o, dO, lse, w.delta, w.lse2, a.B, a.T, a.H, s);
+    if (a.D == 64) launch_pre<float, 64>(o, dO, lse, w.ndelta, w.nlse2, a.B, a.T, a.H, s);
+    else launch_pre<float, 128>(o, dO, lse, w.ndelta, w.nlse2, a.B, a.T, a.H, s);
   }
   return hipGetLastError();
 }
@@ -526,7 +536,7 @@ hipError_t launch_bwd_dkdv(const AttnShape& a, const void* q, const void* k, con
   if (is_bf16) {
     bwdk::Params p;
     p.q = (const bf16*)q; p.k = (const bf16*)k; p.v = (const bf16*)v; p.ve = (const bf16*)ve;
-    p.gate = gate; p.lse2 = w.lse2; p.delta = w.delta; p.dO = (const bf16*)dO;
+    p.gate = gate; p.nlse2 = w.nlse2; p.ndelta = w.ndelta; p.dO = (const bf16*)dO;
     p.dk = (bf16*)dk; p.dv = (bf16*)dv; p.dve = (bf16*)dve; p.dgate = dgate;
     p.B = B; p.T = T; p.H = H; p.window = a.window;
     p.nkb = (T + bwdk::BNK - 1) / bwdk::BNK;
@@ -539,11 +549,11 @@ hipError_t launch_bwd_dkdv(const AttnShape& a, const void* q, const void* k, con
   dim3 grid(T, B * H);
   if (D == 64)
     hipLaunchKernelGGL(bwd_dkdv_f32_kernel<64>, grid, dim3(64), 0, s, (const float*)q, (const float*)k,
-                       (const float*)v, (const float*)ve, gate, lse, w.delta, (const float*)dO,
+                       (const float*)v, (const float*)ve, gate, lse, w.ndelta, (const float*)dO,
                        (float*)dk, (float*)dv, (float*)dve, dgate, T, H, a.window, a.scale);
   else
     hipLaunchKernelGGL(bwd_dkdv_f32_kernel<128>, grid, dim3(64), 0, s, (const float*)q, (const float*)k,
-                       (const float*)v, (const float*)ve, gate, lse, w.delta, (const float*)dO,
+                       (const float*)v, (const float*)ve, gate, lse, w.ndelta, (const float*)dO,
                        (float*)dk, (float*)dv, (float*)dve, dgate, T, H, a.window, a.scale);
   return hipGetLastError();
 }
@@ -553,15 +563,15 @@ hipError_t launch_bwd_dq(const AttnShape& a, const void* q, const void* k, const
                          void* dq, void* ws, bool is_bf16, hipStream_t s) {
   const int B = a.B, T = a.T, H = a.H, D = a.D;
   const WsView w = ws_view(ws, B, T, H);
-  if (is_bf16) return launch_dq_bf16(a, q, k, v, ve, gate, dO, w.lse2, w.delta, dq, s);
+  if (is_bf16) return launch_dq_bf16(a, q, k, v, ve, gate, dO, w.nlse2, w.ndelta, dq, s);
   dim3 grid(T, B * H);
   if (D == 64)
     hipLaunchKernelGGL(bwd_dq_f32_kernel<64>, grid, dim3(64), 0, s, (const float*)q, (const float*)k,
-                       (const float*)v, (const float*)ve, gate, lse, w.delta, (const float*)dO,
+                       (const float*)v, (const float*)ve, gate, lse, w.ndelta, (const float*)dO,
                        (float*)dq, T, H, a.window, a.scale);
   else
     hipLaunchKernelGGL(bwd_dq_f32_kernel<128>, grid, dim3(64), 0, s, (const float*)q, (const float*)k,
-                       (const float*)v, (const float*)ve, gate, lse, w.delta, (const float*)dO,
+                       (const float*)v, (const float*)ve, gate, lse, w.ndelta, (const float*)dO,
                        (float*)dq, T, H, a.window, a.scale);
   return hipGetLastError();
 }

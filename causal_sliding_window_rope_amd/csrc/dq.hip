@@ -31,7 +31,7 @@ template <int D> struct Cfg {
 
 struct Params {
   const bf16* q; const bf16* k; const bf16* v; const bf16* ve; const float* gate;
-  const bf16* dO; const float* lse2; const float* delta;
+  const bf16* dO; const float* nlse2; const float* ndelta;   // row terms, negated
   bf16* dq;
   int B, T, H, window, nqb;
   float c;       // scale * log2(e)
@@ -100,8 +100,8 @@ template <int D>
 __device__ __forceinline__ void dq_tile(f32x16* dqacc, const bf16x8* qreg, const bf16x8* oreg,
                                         const lds_t<bf16>* ks, const lds_t<bf16>* vs,
                                         const int* krow, const int* ktr1, const int* ktr2, int k0,
-                                        int qw, int myq, int T, int W, float c, float l2,
-                                        float dl, int hi) {
+                                        int qw, int myq, int T, int W, float c, float nl2,
+                                        float ndl, int hi) {
   constexpr int NKS = D / 16, NDB = D / 32;
   const bool skip = (k0 > qw + 31) || (k0 + BN - 1 < qw - W + 1);
   if (skip) return;
@@ -122,7 +122,7 @@ __device__ __forceinline__ void dq_tile(f32x16* dqacc, const bf16x8* qreg, const
     sched_fence();
     float pv[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, -l2));
+    for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, nl2));
     if (need_mask) {
       branch_keep();
 #pragma unroll
@@ -138,7 +138,7 @@ __device__ __forceinline__ void dq_tile(f32x16* dqacc, const bf16x8* qreg, const
       for (int jj = 0; jj < 8; jj += 2) {
         const int i = 8 * sp + jj;
         const bf16x2 t = __builtin_convertvector(
-            (f32x2){pv[i] * (dp[i] - dl), pv[i + 1] * (dp[i + 1] - dl)}, bf16x2);
+            (f32x2){pv[i] * (dp[i] + ndl), pv[i + 1] * (dp[i + 1] + ndl)}, bf16x2);
         dsb[sp][jj] = t[0];
         dsb[sp][jj + 1] = t[1];
       }
@@ -200,8 +200,8 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) dq_bf16_kernel(Params p) {
     }
   }
   const size_t rrow = (size_t)bh * T + min(myq, T - 1);
-  const float l2 = p.lse2[rrow];
-  const float dl = p.delta[rrow];
+  const float nl2 = p.nlse2[rrow];
+  const float ndl = p.ndelta[rrow];
 
   const int kt_lo = max(0, q0 - W + 1) / BN;
   const int kt_hi = min(T - 1, q0 + BM - 1) / BN;
@@ -232,12 +232,12 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) dq_bf16_kernel(Params p) {
   __syncthreads();
   for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
     if (kt + 1 <= kt_hi) tl.load(p, kbase, vbase, K1, V1, kt + 1, tid);
-    dq_tile<D>(dqacc, qreg, oreg, K0, V0, krow, ktr1, ktr2, kt * BN, qw, myq, T, W, p.c, l2, dl, hi);
+    dq_tile<D>(dqacc, qreg, oreg, K0, V0, krow, ktr1, ktr2, kt * BN, qw, myq, T, W, p.c, nl2, ndl, hi);
     wait_vmem();
     __syncthreads();
     if (kt + 1 > kt_hi) break;
     if (kt + 2 <= kt_hi) tl.load(p, kbase, vbase, K0, V0, kt + 2, tid);
-    dq_tile<D>(dqacc, qreg, oreg, K1, V1, krow, ktr1, ktr2, (kt + 1) * BN, qw, myq, T, W, p.c, l2, dl, hi);
+    dq_tile<D>(dqacc, qreg, oreg, K1, V1, krow, ktr1, ktr2, (kt + 1) * BN, qw, myq, T, W, p.c, nl2, ndl, hi);
     wait_vmem();
     __syncthreads();
   }
@@ -267,11 +267,11 @@ static hipError_t launch_t(const AttnShape& a, const Params& p, hipStream_t s) {
 }  // namespace dqk
 
 hipError_t launch_dq_bf16(const AttnShape& a, const void* q, const void* k, const void* v,
-                          const void* ve, const float* gate, const void* dO, const float* lse2,
-                          const float* delta, void* dq, hipStream_t s) {
+                          const void* ve, const float* gate, const void* dO, const float* nlse2,
+                          const float* ndelta, void* dq, hipStream_t s) {
   dqk::Params p;
   p.q = (const bf16*)q; p.k = (const bf16*)k; p.v = (const bf16*)v; p.ve = (const bf16*)ve;
-  p.gate = gate; p.dO = (const bf16*)dO; p.lse2 = lse2; p.delta = delta; p.dq = (bf16*)dq;
+  p.gate = gate; p.dO = (const bf16*)dO; p.nlse2 = nlse2; p.ndelta = ndelta; p.dq = (bf16*)dq;
   p.B = a.B; p.T = a.T; p.H = a.H; p.window = a.window;
   p.nqb = (a.T + dqk::BM - 1) / dqk::BM;
   p.c = a.scale * kLog2e;

@@ -31,7 +31,7 @@ hipError_t launch_fwd(const AttnShape& a, const void* q, const void* k, const vo
                       hipStream_t s);
 
 size_t bwd_workspace_bytes(int B, int T, int H, int D, bool bf16);
-// Backward in three stages on one workspace: row terms (delta, lse*log2e), dK/dV (key-block
+// Backward in three stages on one workspace: row terms (-delta, -lse*log2e), dK/dV (key-block
 // major), dQ (query-block major).
 hipError_t launch_bwd_pre(const AttnShape& a, const void* o, const void* dO, const float* lse,
                           void* ws, bool bf16, hipStream_t s);
@@ -43,7 +43,7 @@ hipError_t launch_bwd_dq(const AttnShape& a, const void* q, const void* k, const
                          const void* ve, const float* gate, const float* lse, const void* dO,
                          void* dq, void* ws, bool bf16, hipStream_t s);
 hipError_t launch_dq_bf16(const AttnShape& a, const void* q, const void* k, const void* v,
-                          const void* ve, const float* gate, const void* dO, const float* lse2,
-                          const float* delta, void* dq, hipStream_t s);
+                          const void* ve, const float* gate, const void* dO, const float* nlse2,
+                          const float* ndelta, void* dq, hipStream_t s);
 
 }  // namespace swa

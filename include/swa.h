@@ -139,7 +139,7 @@ int swa_fwd(const void* q, const void* k, const void* v, const void* ve, const f
             void* o, float* lse, int B, int T, int H, int D, int window, float scale,
             swa_dtype dtype, void* stream);
 
-/* Bytes of workspace swa_bwd needs: the row terms delta and lse*log2(e), each (B,H,T) float32,
+/* Bytes of workspace swa_bwd needs: the row terms -delta and -lse*log2(e), each (B,H,T) float32,
  * 256-byte aligned inside the block and followed by 512 bytes of slack. */
 size_t swa_bwd_workspace_size(int B, int T, int H, int D, swa_dtype dtype);
 
@@ -163,7 +163,8 @@ int swa_bwd(const void* q, const void* k, const void* v, const void* ve, const f
  * The three stages swa_bwd runs, for callers that schedule or time them separately. Call them
  * in this order on one stream with one workspace (same sizes and dtype throughout):
  *
- * swa_bwd_preprocess — delta_i = dO_i . O_i and lse_i * log2(e) into the workspace.
+ * swa_bwd_preprocess — the row terms -delta_i = -dO_i . O_i and -lse_i * log2(e) into the
+ *   workspace (stored negated: the bf16 kernels start their accumulators from them).
  */
 int swa_bwd_preprocess(const void* o, const void* dO, const float* lse, void* workspace,
                        size_t ws_bytes, int B, int T, int H, int D, swa_dtype dtype, void* stream);
