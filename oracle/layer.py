@@ -22,7 +22,7 @@ from .attention import attention_fwd, attention_bwd
 
 
 def layer_fwd(q, k, v, window, *, base=10000.0, eps=1e-6, scale=None, x32=None, Wg=None, ve=None,
-              round_boundary=False):
+              round_boundary=False, doc_id=None):
     D = q.shape[-1]
     scale = 1.0 / np.sqrt(D) if scale is None else scale
     qh, rq = rope_qknorm(q, base, eps)
@@ -37,18 +37,18 @@ def layer_fwd(q, k, v, window, *, base=10000.0, eps=1e-6, scale=None, x32=None, 
     else:
         v_eff = v
     out["v_eff"] = v_eff
-    O, lse = attention_fwd(qh, kh, v_eff, window, scale)
+    O, lse = attention_fwd(qh, kh, v_eff, window, scale, doc_id=doc_id)
     out["O"], out["lse"] = O, lse
     return out
 
 
 def layer_bwd(q, k, v, dO, window, fwd, *, base=10000.0, eps=1e-6, scale=None, x32=None, Wg=None,
-              ve=None):
+              ve=None, doc_id=None):
     """Gradients w.r.t. the pre-RoPE q, k, the raw v (and ve, Wg, x32 with the gate)."""
     D = q.shape[-1]
     scale = 1.0 / np.sqrt(D) if scale is None else scale
     dqh, dkh, dv_eff = attention_bwd(fwd["qh"], fwd["kh"], fwd["v_eff"], dO, window, scale,
-                                     lse=fwd["lse"])
+                                     lse=fwd["lse"], doc_id=doc_id)
     out = {"dqh": dqh, "dkh": dkh, "dv_eff": dv_eff}
     out["dq"] = rope_qknorm_bwd(q, dqh, base, eps)
     out["dk"] = rope_qknorm_bwd(k, dkh, base, eps)
