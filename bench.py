@@ -46,8 +46,37 @@ def layer_list(name: str):
                          "(18 x 1024, 6 x 2048), B=16, T=2048, H=12, D=128")
     wl = WORKLOADS[name]
     return dict(B=wl.B, T=wl.T, H=wl.H, D=wl.D, gate=wl.gate, windows=[wl.window],
+                doc_mean=wl.doc_mean, seed=wl.seed,
                 desc=f"{name}: B={wl.B}, T={wl.T}, H={wl.H}, D={wl.D}, window {wl.window}"
-                     + (", value-embedding gate" if wl.gate else ""))
+                     + (", value-embedding gate" if wl.gate else "")
+                     + (f", packed rows of documents averaging {wl.doc_mean} tokens"
+                        if wl.doc_mean else ""))
+
+
+def doc_starts(cfg):
+    """(B, T) start of each token's document for document-masked workloads, else None."""
+    import numpy as np
+    from causal_sliding_window_rope_amd.inputs import doc_layout
+    if not cfg.get("doc_mean"):
+        return None, None
+    ids = doc_layout(np.random.default_rng(cfg["seed"]), cfg["B"], cfg["T"], cfg["doc_mean"])
+    starts = np.zeros_like(ids)
+    for b in range(ids.shape[0]):
+        change = np.ones(ids.shape[1], dtype=bool)
+        change[1:] = ids[b, 1:] != ids[b, :-1]
+        pos = np.where(change, np.arange(ids.shape[1]), 0)
+        starts[b] = np.maximum.accumulate(pos)
+    return ids, starts
+
+
+def visible_pairs(cfg, W, starts):
+    """Visible (query, key) pairs per head summed over the batch."""
+    import numpy as np
+    B, T = cfg["B"], cfg["T"]
+    if starts is None:
+        return pairs(T, W) * B
+    i = np.arange(T)[None, :]
+    return int(np.minimum(i - starts + 1, W).sum())
 
 
 def make_layers(cfg, torch, seed0=1000):
@@ -84,6 +113,12 @@ def run_bench(args):
     B, T, H, D = cfg["B"], cfg["T"], cfg["H"], cfg["D"]
     scale = D ** -0.5
     layers = make_layers(cfg, torch)
+    doc_ids, starts = doc_starts(cfg)
+    if doc_ids is not None:
+        # one document layout per batch, shared by every layer (as in a training step)
+        bounds_t = sw.swa_doc_bounds(torch.from_numpy(doc_ids).cuda())
+        for t in layers:
+            t["bounds"] = bounds_t
     cs = sw.rope_table(T, D, 10000.0)
     # gradient buffers shared by all layers
     g = {n: torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
@@ -108,6 +143,7 @@ def run_bench(args):
     def step(rec):
         # forward, layers in order
         for li, t in enumerate(layers):
+            bounds = t.get("bounds")
             call("rope_qknorm_fwd", P(t["q"]), P(t["k"]), P(cs), P(t["qn"]), P(t["kn"]), B, T, H, D,
                  1e-6, sw.SWA_BF16, stream)
             ve = gate = None
@@ -116,12 +152,14 @@ def run_bench(args):
                      H, D, sw.SWA_BF16, stream)
                 ve, gate = t["ve"], t["gate"]
             if rec: rec["fwd"][li][0].record()
-            call("swa_fwd", P(t["qn"]), P(t["kn"]), P(t["v"]), P(ve), P(gate), P(t["o"]), P(t["lse"]),
+            call("swa_fwd", P(t["qn"]), P(t["kn"]), P(t["v"]), P(ve), P(gate), P(bounds), P(t["o"]),
+                 P(t["lse"]),
                  B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
             if rec: rec["fwd"][li][1].record()
         # backward, layers in reverse
         for li in reversed(range(len(layers))):
             t = layers[li]
+            bounds = t.get("bounds")
             ve = gate = dve = dgate = None
             if cfg["gate"]:
                 ve, gate, dve, dgate = t["ve"], t["gate"], g["dve"], g["dgate"]
@@ -129,11 +167,13 @@ def run_bench(args):
             call("swa_bwd_preprocess", P(t["o"]), P(t["dO"]), P(t["lse"]), P(ws), nws, B, T, H, D,
                  sw.SWA_BF16, stream)
             if rec: rec["bwd"][li][1].record()
-            call("swa_bwd_dkdv", P(t["qn"]), P(t["kn"]), P(t["v"]), P(ve), P(gate), P(t["lse"]),
+            call("swa_bwd_dkdv", P(t["qn"]), P(t["kn"]), P(t["v"]), P(ve), P(gate), P(bounds),
+                 P(t["lse"]),
                  P(t["dO"]), P(g["dkn"]), P(g["dv"]), P(dve), P(dgate), P(ws), nws,
                  B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
             if rec: rec["bwd"][li][2].record()
-            call("swa_bwd_dq", P(t["qn"]), P(t["kn"]), P(t["v"]), P(ve), P(gate), P(t["lse"]),
+            call("swa_bwd_dq", P(t["qn"]), P(t["kn"]), P(t["v"]), P(ve), P(gate), P(bounds),
+                 P(t["lse"]),
                  P(t["dO"]), P(g["dqn"]), P(ws), nws, B, T, H, D, t["W"], scale, sw.SWA_BF16,
                  stream)
             if rec: rec["bwd"][li][3].record()
@@ -166,7 +206,7 @@ def run_bench(args):
     dq_ms = sum(r["bwd"][l][2].elapsed_time(r["bwd"][l][3]) for r in recs for l in range(nl))
     launches = args.steps * nl
 
-    npairs = sum(pairs(T, W) for W in cfg["windows"]) * B * H
+    npairs = sum(visible_pairs(cfg, W, starts) for W in cfg["windows"]) * H
     fwd_flop = 4 * D * npairs
     bwd_flop = 10 * D * npairs
     flop = fwd_flop + bwd_flop
@@ -275,14 +315,19 @@ def cpu_baseline(args):
     hcount = 0
     while secs < args.cpu_seconds and hcount < 512:
         W = wins[hcount % len(wins)]
-        wl = small_workload(1, T, 1, D, W, "bf16", seed=9000 + hcount)
+        wl = small_workload(1, T, 1, D, W, "bf16", seed=9000 + hcount,
+                            doc_mean=cfg.get("doc_mean") or 0)
         x = make_inputs(wl)
         f = {n: x[n].astype(np.float64) for n in ("q", "k", "v", "dO")}
+        doc = x.get("doc_id")
         t0 = time.perf_counter()
-        fwd = oracle.layer_fwd(f["q"], f["k"], f["v"], W, round_boundary=True)
-        oracle.layer_bwd(f["q"], f["k"], f["v"], f["dO"], W, fwd)
+        fwd = oracle.layer_fwd(f["q"], f["k"], f["v"], W, round_boundary=True, doc_id=doc)
+        oracle.layer_bwd(f["q"], f["k"], f["v"], f["dO"], W, fwd, doc_id=doc)
         secs += time.perf_counter() - t0
-        done_flop += 14 * D * pairs(T, W)
+        if doc is None:
+            done_flop += 14 * D * pairs(T, W)
+        else:
+            done_flop += 14 * D * int(oracle.visible_mask(T, W, oracle.segment_ids(doc)[0]).sum())
         heads[W] = heads.get(W, 0) + 1
         hcount += 1
     sample = ", ".join(f"{n} head(s) of T={T}, D={D}, window {w}" for w, n in sorted(heads.items()))
@@ -299,7 +344,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="sssl24",
-                    choices=["sssl24", "d24_short", "d24_full", "gpt2_124m", "d24_short_ve"])
+                    choices=["sssl24", "d24_short", "d24_full", "gpt2_124m", "d24_short_ve",
+                             "d24_short_doc"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",

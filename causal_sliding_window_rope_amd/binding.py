@@ -32,14 +32,16 @@ SIGNATURES = {
     "rope_qknorm_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "ve_gate_v": (_I, [_P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "ve_gate_v_bwd": (_I, [_P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
-    "swa_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "swa_doc_bounds": (_I, [_P, _P, _I, _I, _P]),
+    "swa_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "swa_bwd_workspace_size": (_S, [_I, _I, _I, _I, _I]),
-    "swa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
+    "swa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
                      _I, _I, _I, _I, _I, _F, _I, _P]),
     "swa_bwd_preprocess": (_I, [_P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _P]),
-    "swa_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
+    "swa_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
                           _I, _I, _I, _I, _I, _F, _I, _P]),
-    "swa_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "swa_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _F, _I,
+                        _P]),
 }
 
 _lib = None
@@ -160,8 +162,17 @@ def ve_gate_v_bwd(x, Wg, gate, dgate, want_dx32: bool = True):
     return dWg, dx32
 
 
+def swa_doc_bounds(doc_id, out=None):
+    """Per-token [start, end) of each token's document (maximal run of equal ids), (B, T, 2)."""
+    B, T = doc_id.shape
+    _check(doc_id, "doc_id", (B, T), torch.int32)
+    bounds = torch.empty((B, T, 2), dtype=torch.int32, device=doc_id.device) if out is None else out
+    _call("swa_doc_bounds", _ptr(doc_id), _ptr(bounds), B, T, _stream())
+    return bounds
+
+
 def swa_fwd(q, k, v, window: int, scale: float | None = None, ve=None, gate=None, out=None,
-            lse=None):
+            lse=None, doc_bounds=None):
     B, T, H, D = q.shape
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _check(t, n, (B, T, H, D), q.dtype)
@@ -171,8 +182,10 @@ def swa_fwd(q, k, v, window: int, scale: float | None = None, ve=None, gate=None
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if lse is None else lse
-    _call("swa_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), _ptr(o), _ptr(lse), B, T, H,
-          D, int(window), float(scale), _dt(q), _stream())
+    if doc_bounds is not None:
+        _check(doc_bounds, "doc_bounds", (B, T, 2), torch.int32)
+    _call("swa_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), _ptr(doc_bounds), _ptr(o),
+          _ptr(lse), B, T, H, D, int(window), float(scale), _dt(q), _stream())
     return o, lse
 
 
@@ -181,7 +194,7 @@ def swa_bwd_workspace_size(B: int, T: int, H: int, D: int, dtype: torch.dtype) -
 
 
 def swa_bwd(q, k, v, o, lse, dO, window: int, scale: float | None = None, ve=None, gate=None,
-            workspace=None, grads=None):
+            workspace=None, grads=None, doc_bounds=None):
     """Returns (dq, dk, dv) or, with the gate, (dq, dk, dv, dve, dgate)."""
     B, T, H, D = q.shape
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dO, "dO")):
@@ -197,7 +210,10 @@ def swa_bwd(q, k, v, o, lse, dO, window: int, scale: float | None = None, ve=Non
         dgate = torch.empty((B, T, H), dtype=torch.float32, device=q.device) if ve is not None else None
     else:
         dq, dk, dv, dve, dgate = grads
-    _call("swa_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), _ptr(o), _ptr(lse), _ptr(dO),
+    if doc_bounds is not None:
+        _check(doc_bounds, "doc_bounds", (B, T, 2), torch.int32)
+    _call("swa_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), _ptr(doc_bounds), _ptr(o),
+          _ptr(lse), _ptr(dO),
           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dve), _ptr(dgate), _ptr(workspace),
           workspace.numel() * workspace.element_size(), B, T, H, D, int(window), float(scale),
           _dt(q), _stream())
@@ -207,7 +223,7 @@ def swa_bwd(q, k, v, o, lse, dO, window: int, scale: float | None = None, ve=Non
 
 
 def swa_bwd_stages(q, k, v, o, lse, dO, window: int, scale: float | None = None, ve=None,
-                   gate=None, workspace=None, grads=None):
+                   gate=None, workspace=None, grads=None, doc_bounds=None):
     """swa_bwd as its three C-ABI stages: preprocess, dK/dV, dQ."""
     B, T, H, D = q.shape
     scale = 1.0 / math.sqrt(D) if scale is None else scale
@@ -225,10 +241,12 @@ def swa_bwd_stages(q, k, v, o, lse, dO, window: int, scale: float | None = None,
     dt = _dt(q)
     _call("swa_bwd_preprocess", _ptr(o), _ptr(dO), _ptr(lse), _ptr(workspace), nbytes, B, T, H, D, dt,
           st)
-    _call("swa_bwd_dkdv", _ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), _ptr(lse), _ptr(dO),
+    _call("swa_bwd_dkdv", _ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), _ptr(doc_bounds),
+          _ptr(lse), _ptr(dO),
           _ptr(dk), _ptr(dv), _ptr(dve), _ptr(dgate), _ptr(workspace), nbytes, B, T, H, D,
           int(window), float(scale), dt, st)
-    _call("swa_bwd_dq", _ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), _ptr(lse), _ptr(dO),
+    _call("swa_bwd_dq", _ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), _ptr(doc_bounds),
+          _ptr(lse), _ptr(dO),
           _ptr(dq), _ptr(workspace), nbytes, B, T, H, D, int(window), float(scale), dt, st)
     if ve is not None:
         return dq, dk, dv, dve, dgate

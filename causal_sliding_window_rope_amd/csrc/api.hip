@@ -160,17 +160,29 @@ int ve_gate_v_bwd(const void* x, int ldx, const float* Wg, const float* gate, co
                                             dtype == SWA_BF16, (hipStream_t)stream), fn);
 }
 
-int swa_fwd(const void* q, const void* k, const void* v, const void* ve, const float* gate, void* o,
-            float* lse, int B, int T, int H, int D, int window, float scale, swa_dtype dtype,
-            void* stream) {
+int swa_doc_bounds(const int* doc_id, int* doc_bounds, int B, int T, void* stream) {
+  const char* fn = "swa_doc_bounds";
+  SWA_TRY(need(fn, "doc_id", doc_id));
+  SWA_TRY(need(fn, "doc_bounds", doc_bounds));
+  if (B < 1 || T < 1) return fail(SWA_ERR_INVALID_ARG, "%s: B and T must be >= 1", fn);
+  if ((long long)B * T >= (1LL << 30))
+    return fail(SWA_ERR_UNSUPPORTED, "%s: B*T exceeds the supported index range", fn);
+  if (doc_bounds == doc_id) return fail(SWA_ERR_INVALID_ARG, "%s: doc_bounds may not alias doc_id", fn);
+  return hip_status(swa::launch_doc_bounds(doc_id, doc_bounds, B, T, (hipStream_t)stream), fn);
+}
+
+int swa_fwd(const void* q, const void* k, const void* v, const void* ve, const float* gate,
+            const int* doc_bounds, void* o, float* lse, int B, int T, int H, int D, int window,
+            float scale, swa_dtype dtype, void* stream) {
   const char* fn = "swa_fwd";
   SWA_TRY(check_shape(fn, B, T, H, D, dtype));
   SWA_TRY(need(fn, "q", q)); SWA_TRY(need(fn, "k", k)); SWA_TRY(need(fn, "v", v));
   SWA_TRY(need(fn, "o", o)); SWA_TRY(need(fn, "lse", lse));
   if ((ve == nullptr) != (gate == nullptr))
     return fail(SWA_ERR_INVALID_ARG, "%s: ve and gate must be given together", fn);
-  SWA_TRY(opt(fn, "ve", ve));
+  SWA_TRY(opt(fn, "ve", ve)); SWA_TRY(opt(fn, "doc_bounds", doc_bounds));
   swa::AttnShape a{B, T, H, D, 0, scale};
+  a.bounds = doc_bounds;
   SWA_TRY(check_window_scale(fn, window, scale, T, &a.window));
   return hip_status(swa::launch_fwd(a, q, k, v, ve, gate, o, lse, dtype == SWA_BF16,
                                     (hipStream_t)stream), fn);
@@ -182,7 +194,8 @@ size_t swa_bwd_workspace_size(int B, int T, int H, int D, swa_dtype dtype) {
 }
 
 static int check_bwd(const char* fn, const void* q, const void* k, const void* v, const void* ve,
-                     const float* gate, const void* o, const float* lse, const void* dO,
+                     const float* gate, const int* doc_bounds, const void* o, const float* lse,
+                     const void* dO,
                      const void* dq, const void* dk, const void* dv, const void* dve,
                      const float* dgate, const void* workspace, size_t ws_bytes, int B, int T,
                      int H, int D, int window, float scale, swa_dtype dtype, swa::AttnShape* a) {
@@ -197,19 +210,21 @@ static int check_bwd(const char* fn, const void* q, const void* k, const void* v
   if (g != (dve != nullptr) || g != (dgate != nullptr))
     return fail(SWA_ERR_INVALID_ARG, "%s: dve and dgate are required with the gate, NULL without", fn);
   SWA_TRY(opt(fn, "ve", ve)); SWA_TRY(opt(fn, "dve", dve));
+  SWA_TRY(opt(fn, "doc_bounds", doc_bounds));
   *a = swa::AttnShape{B, T, H, D, 0, scale};
+  a->bounds = doc_bounds;
   SWA_TRY(check_window_scale(fn, window, scale, T, &a->window));
   return check_ws(fn, workspace, ws_bytes, B, T, H, D, dtype);
 }
 
 int swa_bwd(const void* q, const void* k, const void* v, const void* ve, const float* gate,
-            const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
-            void* dve, float* dgate, void* workspace, size_t ws_bytes, int B, int T, int H, int D,
-            int window, float scale, swa_dtype dtype, void* stream) {
+            const int* doc_bounds, const void* o, const float* lse, const void* dO, void* dq,
+            void* dk, void* dv, void* dve, float* dgate, void* workspace, size_t ws_bytes, int B,
+            int T, int H, int D, int window, float scale, swa_dtype dtype, void* stream) {
   const char* fn = "swa_bwd";
   swa::AttnShape a;
   SWA_TRY(need(fn, "o", o));
-  SWA_TRY(check_bwd(fn, q, k, v, ve, gate, o, lse, dO, dq, dk, dv, dve, dgate, workspace,
+  SWA_TRY(check_bwd(fn, q, k, v, ve, gate, doc_bounds, o, lse, dO, dq, dk, dv, dve, dgate, workspace,
                     ws_bytes, B, T, H, D, window, scale, dtype, &a));
   const bool bf = dtype == SWA_BF16;
   const hipStream_t s = (hipStream_t)stream;
@@ -231,29 +246,31 @@ int swa_bwd_preprocess(const void* o, const void* dO, const float* lse, void* wo
 }
 
 int swa_bwd_dkdv(const void* q, const void* k, const void* v, const void* ve, const float* gate,
-                 const float* lse, const void* dO, void* dk, void* dv, void* dve, float* dgate,
-                 void* workspace, size_t ws_bytes, int B, int T, int H, int D, int window,
-                 float scale, swa_dtype dtype, void* stream) {
+                 const int* doc_bounds, const float* lse, const void* dO, void* dk, void* dv,
+                 void* dve, float* dgate, void* workspace, size_t ws_bytes, int B, int T, int H,
+                 int D, int window, float scale, swa_dtype dtype, void* stream) {
   const char* fn = "swa_bwd_dkdv";
   swa::AttnShape a;
   // dq is not used by this stage; dk stands in for it in the shared checks
-  SWA_TRY(check_bwd(fn, q, k, v, ve, gate, nullptr, lse, dO, dk, dk, dv, dve, dgate, workspace,
+  SWA_TRY(check_bwd(fn, q, k, v, ve, gate, doc_bounds, nullptr, lse, dO, dk, dk, dv, dve, dgate, workspace,
                     ws_bytes, B, T, H, D, window, scale, dtype, &a));
   return hip_status(swa::launch_bwd_dkdv(a, q, k, v, ve, gate, lse, dO, dk, dv, dve, dgate,
                                          workspace, dtype == SWA_BF16, (hipStream_t)stream), fn);
 }
 
 int swa_bwd_dq(const void* q, const void* k, const void* v, const void* ve, const float* gate,
-               const float* lse, const void* dO, void* dq, void* workspace, size_t ws_bytes, int B,
-               int T, int H, int D, int window, float scale, swa_dtype dtype, void* stream) {
+               const int* doc_bounds, const float* lse, const void* dO, void* dq, void* workspace,
+               size_t ws_bytes, int B, int T, int H, int D, int window, float scale,
+               swa_dtype dtype, void* stream) {
   const char* fn = "swa_bwd_dq";
   SWA_TRY(check_shape(fn, B, T, H, D, dtype));
   SWA_TRY(need(fn, "q", q)); SWA_TRY(need(fn, "k", k)); SWA_TRY(need(fn, "v", v));
   SWA_TRY(need(fn, "lse", lse)); SWA_TRY(need(fn, "dO", dO)); SWA_TRY(need(fn, "dq", dq));
   if ((ve != nullptr) != (gate != nullptr))
     return fail(SWA_ERR_INVALID_ARG, "%s: ve and gate must be given together", fn);
-  SWA_TRY(opt(fn, "ve", ve));
+  SWA_TRY(opt(fn, "ve", ve)); SWA_TRY(opt(fn, "doc_bounds", doc_bounds));
   swa::AttnShape a{B, T, H, D, 0, scale};
+  a.bounds = doc_bounds;
   SWA_TRY(check_window_scale(fn, window, scale, T, &a.window));
   SWA_TRY(check_ws(fn, workspace, ws_bytes, B, T, H, D, dtype));
   return hip_status(swa::launch_bwd_dq(a, q, k, v, ve, gate, lse, dO, dq, workspace,

@@ -85,6 +85,7 @@ template <int D> struct Cfg {
 struct Params {
   const bf16* q; const bf16* k; const bf16* v; const bf16* ve; const float* gate;
   const float* nlse2; const float* ndelta; const bf16* dO;   // row terms, negated
+  const int* bounds;   // per-token document [start, end) (document masking only)
   bf16* dk; bf16* dv; bf16* dve; float* dgate;
   int B, T, H, window, nkb;
   float c;       // scale * log2(e)
@@ -116,7 +117,7 @@ __device__ __forceinline__ void load_qtile(const Params& p, const bf16* qbase, c
   }
 }
 
-template <int D, bool GATE>
+template <int D, bool GATE, bool DOC>
 __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dkdv_bf16_kernel(Params p) {
   using C = Cfg<D>;
   constexpr int NDB = D / 32, NKS = D / 16;
@@ -187,8 +188,22 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dkdv_bf16_kernel(Params 
 #pragma unroll
   for (int i = 0; i < NDB; ++i) { dv[i] = (f32x16){}; dk[i] = (f32x16){}; }
 
+  // Queries that see this lane's key: [key, hi_key] (window, sequence end and, with document
+  // masking, the end of the key's document); whi0 / whi1: hi_key of the wave's first and last
+  // key (hi_key never decreases along a row).
+  const int kc = min(mykey, T - 1);
+  int kend = T;
+  if constexpr (DOC) kend = p.bounds[2 * ((size_t)b * T + kc) + 1];
+  const int hi_key = min(kc + W - 1, kend - 1);
+  const int whi0 = __builtin_amdgcn_readlane(hi_key, 0);
+  const int whi1 = __builtin_amdgcn_readlane(hi_key, 31);
+  int hi_wg = min(T - 1, kb0 + BNK - 1 + W - 1);   // last query any key of the workgroup sees
+  if constexpr (DOC) {
+    const int kl = min(kb0 + BNK - 1, T - 1);
+    hi_wg = min(kl + W - 1, p.bounds[2 * ((size_t)b * T + kl) + 1] - 1);
+  }
   const int qt_lo = kb0 / BMQ;
-  const int qt_hi = min(T - 1, kb0 + BNK - 1 + W - 1) / BMQ;
+  const int qt_hi = hi_wg / BMQ;
 
   // Lane-constant LDS element offsets: every swizzled address below is one of these plus a
   // compile-time row offset, so the LDS loads use immediate offsets off a few registers.
@@ -204,8 +219,8 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dkdv_bf16_kernel(Params 
     trb1[db] = r1 * D + 8 * ((d >> 3) ^ swz<D>(r1)) + 4 * ((d >> 2) & 1);
     trb2[db] = r2 * D + 8 * ((d >> 3) ^ swz<D>(r2)) + 4 * ((d >> 2) & 1);
   }
-  // number of queries (from the key itself on) that see this lane's key: min(W, T - key)
-  const unsigned mask_n = mykey < T ? (unsigned)min(W, T - mykey) : 0u;
+  // number of queries (from the key itself on) that see this lane's key
+  const unsigned mask_n = mykey < T ? (unsigned)(hi_key - mykey + 1) : 0u;
 
   // One query tile: recompute S, P, dP, dS in 32-query halves; accumulate dV and dK.
   auto tile = [&](const lds_t<bf16>* Qs, const lds_t<bf16>* Os, const lds_t<float>* Ls,
@@ -214,9 +229,9 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dkdv_bf16_kernel(Params 
 #pragma unroll
     for (int mb = 0; mb < BMQ / 32; ++mb) {
       const int qm = q0 + 32 * mb;
-      const bool skip = (qm + 31 < kw) || (qm > kw + 31 + W - 1) || (kw >= T);
+      const bool skip = (qm + 31 < kw) || (qm > whi1) || (kw >= T);
       if (skip) continue;
-      const bool need_mask = (qm < kw + 31) || (qm + 31 > kw + W - 1) || (qm + 32 > T) ||
+      const bool need_mask = (qm < kw + 31) || (qm + 31 > whi0) || (qm + 32 > T) ||
                              (kw + 32 > T);
       // The LDS operands of each phase are requested together, one phase ahead where registers
       // allow, so the reads overlap one another and the MFMAs of the previous phase; the waits
@@ -385,9 +400,9 @@ template <int D>
 __global__ void __launch_bounds__(64) bwd_dkdv_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ ve, const float* __restrict__ gate, const float* __restrict__ lse,
-    const float* __restrict__ ndelta, const float* __restrict__ dO, float* __restrict__ dk,
-    float* __restrict__ dv, float* __restrict__ dve, float* __restrict__ dgate, int T, int H,
-    int W, float scale) {
+    const float* __restrict__ ndelta, const float* __restrict__ dO, const int* __restrict__ bounds,
+    float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dve,
+    float* __restrict__ dgate, int T, int H, int W, float scale) {
   constexpr int PER = D / 64;
   const int j = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, lane = threadIdx.x;
   const size_t krow = ((size_t)b * T + j) * H + h;
@@ -400,7 +415,8 @@ __global__ void __launch_bounds__(64) bwd_dkdv_f32_kernel(
     if (gate) vv[e] = fmaf(g, ve[krow * D + lane + 64 * e], vv[e]);
     ak[e] = 0.f; av[e] = 0.f;
   }
-  for (int i = j; i <= min(T - 1, j + W - 1); ++i) {
+  const int i1 = min(min(T - 1, j + W - 1), bounds ? bounds[2 * ((size_t)b * T + j) + 1] - 1 : T - 1);
+  for (int i = j; i <= i1; ++i) {
     const size_t qrow = ((size_t)b * T + i) * H + h;
     const float s = wave_dot<D>(kv, q + qrow * D, lane) * scale;
     const float pij = expf(s - lse[(size_t)bh * T + i]);
@@ -433,8 +449,8 @@ template <int D>
 __global__ void __launch_bounds__(64) bwd_dq_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ ve, const float* __restrict__ gate, const float* __restrict__ lse,
-    const float* __restrict__ ndelta, const float* __restrict__ dO, float* __restrict__ dq, int T,
-    int H, int W, float scale) {
+    const float* __restrict__ ndelta, const float* __restrict__ dO, const int* __restrict__ bounds,
+    float* __restrict__ dq, int T, int H, int W, float scale) {
   constexpr int PER = D / 64;
   const int i = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, lane = threadIdx.x;
   const size_t qrow = ((size_t)b * T + i) * H + h;
@@ -446,7 +462,8 @@ __global__ void __launch_bounds__(64) bwd_dq_f32_kernel(
     aq[e] = 0.f;
   }
   const float L = lse[(size_t)bh * T + i], ndl = ndelta[(size_t)bh * T + i];
-  for (int j = max(0, i - W + 1); j <= i; ++j) {
+  const int j0 = max(max(0, i - W + 1), bounds ? bounds[2 * ((size_t)b * T + i)] : 0);
+  for (int j = j0; j <= i; ++j) {
     const size_t krow = ((size_t)b * T + j) * H + h;
     const float s = wave_dot<D>(qv, k + krow * D, lane) * scale;
     const float pij = expf(s - L);
@@ -496,7 +513,10 @@ static void launch_pre(const void* o, const void* dO, const float* lse, float* n
 template <int D, bool GATE>
 static hipError_t launch_dkdv_bf16_t(const AttnShape& a, const bwdk::Params& p, hipStream_t s) {
   const unsigned blocks = (unsigned)p.nkb * a.B * a.H;
-  hipLaunchKernelGGL((bwdk::dkdv_bf16_kernel<D, GATE>), dim3(blocks), dim3(256), 0, s, p);
+  if (a.bounds)
+    hipLaunchKernelGGL((bwdk::dkdv_bf16_kernel<D, GATE, true>), dim3(blocks), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((bwdk::dkdv_bf16_kernel<D, GATE, false>), dim3(blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -537,6 +557,7 @@ hipError_t launch_bwd_dkdv(const AttnShape& a, const void* q, const void* k, con
     bwdk::Params p;
     p.q = (const bf16*)q; p.k = (const bf16*)k; p.v = (const bf16*)v; p.ve = (const bf16*)ve;
     p.gate = gate; p.nlse2 = w.nlse2; p.ndelta = w.ndelta; p.dO = (const bf16*)dO;
+    p.bounds = a.bounds;
     p.dk = (bf16*)dk; p.dv = (bf16*)dv; p.dve = (bf16*)dve; p.dgate = dgate;
     p.B = B; p.T = T; p.H = H; p.window = a.window;
     p.nkb = (T + bwdk::BNK - 1) / bwdk::BNK;
@@ -550,11 +571,11 @@ hipError_t launch_bwd_dkdv(const AttnShape& a, const void* q, const void* k, con
   if (D == 64)
     hipLaunchKernelGGL(bwd_dkdv_f32_kernel<64>, grid, dim3(64), 0, s, (const float*)q, (const float*)k,
                        (const float*)v, (const float*)ve, gate, lse, w.ndelta, (const float*)dO,
-                       (float*)dk, (float*)dv, (float*)dve, dgate, T, H, a.window, a.scale);
+                       a.bounds, (float*)dk, (float*)dv, (float*)dve, dgate, T, H, a.window, a.scale);
   else
     hipLaunchKernelGGL(bwd_dkdv_f32_kernel<128>, grid, dim3(64), 0, s, (const float*)q, (const float*)k,
                        (const float*)v, (const float*)ve, gate, lse, w.ndelta, (const float*)dO,
-                       (float*)dk, (float*)dv, (float*)dve, dgate, T, H, a.window, a.scale);
+                       a.bounds, (float*)dk, (float*)dv, (float*)dve, dgate, T, H, a.window, a.scale);
   return hipGetLastError();
 }
 
@@ -568,11 +589,11 @@ hipError_t launch_bwd_dq(const AttnShape& a, const void* q, const void* k, const
   if (D == 64)
     hipLaunchKernelGGL(bwd_dq_f32_kernel<64>, grid, dim3(64), 0, s, (const float*)q, (const float*)k,
                        (const float*)v, (const float*)ve, gate, lse, w.ndelta, (const float*)dO,
-                       (float*)dq, T, H, a.window, a.scale);
+                       a.bounds, (float*)dq, T, H, a.window, a.scale);
   else
     hipLaunchKernelGGL(bwd_dq_f32_kernel<128>, grid, dim3(64), 0, s, (const float*)q, (const float*)k,
                        (const float*)v, (const float*)ve, gate, lse, w.ndelta, (const float*)dO,
-                       (float*)dq, T, H, a.window, a.scale);
+                       a.bounds, (float*)dq, T, H, a.window, a.scale);
   return hipGetLastError();
 }
 

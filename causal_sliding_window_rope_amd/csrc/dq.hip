@@ -31,6 +31,7 @@ template <int D> struct Cfg {
 
 struct Params {
   const bf16* q; const bf16* k; const bf16* v; const bf16* ve; const float* gate;
+  const int* bounds;   // per-token document [start, end) (document masking only)
   const bf16* dO; const float* nlse2; const float* ndelta;   // row terms, negated
   bf16* dq;
   int B, T, H, window, nqb;
@@ -100,14 +101,15 @@ template <int D>
 __device__ __forceinline__ void dq_tile(f32x16* dqacc, const bf16x8* qreg, const bf16x8* oreg,
                                         const lds_t<bf16>* ks, const lds_t<bf16>* vs,
                                         const int* krow, const int* ktr1, const int* ktr2, int k0,
-                                        int qw, int myq, int T, int W, float c, float nl2,
-                                        float ndl, int hi) {
+                                        int qw, int T, int lo_row, unsigned n, int wlo0, int wlo1,
+                                        float c, float nl2, float ndl, int hi) {
   constexpr int NKS = D / 16, NDB = D / 32;
-  const bool skip = (k0 > qw + 31) || (k0 + BN - 1 < qw - W + 1);
+  // visible keys of this lane's query row: [lo_row, lo_row + n); wlo0 / wlo1: lo_row of the
+  // wave's first and last query (lo_row never decreases along a row)
+  const bool skip = (k0 > qw + 31) || (k0 + BN - 1 < wlo0);
   if (skip) return;
-  const bool need_mask = (k0 + BN - 1 > qw) || (k0 < qw + 31 - W + 1) || (k0 + BN > T);
-  const int lo = max(myq - W + 1, 0) - k0 - 4 * hi;
-  const unsigned n = (unsigned)(min(myq, T - 1) - max(myq - W + 1, 0) + 1);
+  const bool need_mask = (k0 + BN - 1 > qw) || (k0 < wlo1) || (k0 + BN > T);
+  const int lo = lo_row - k0 - 4 * hi;
   // the two 32-key halves of the tile one after the other (halves the live registers)
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -158,7 +160,7 @@ __device__ __forceinline__ void dq_tile(f32x16* dqacc, const bf16x8* qreg, const
   }
 }
 
-template <int D, bool GATE>
+template <int D, bool GATE, bool DOC>
 __global__ void __launch_bounds__(64 * NW, 8 / NW) dq_bf16_kernel(Params p) {
   using C = Cfg<D>;
   constexpr int NDB = D / 32, NKS = D / 16;
@@ -203,7 +205,16 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) dq_bf16_kernel(Params p) {
   const float nl2 = p.nlse2[rrow];
   const float ndl = p.ndelta[rrow];
 
-  const int kt_lo = max(0, q0 - W + 1) / BN;
+  const int qc = min(myq, T - 1);
+  int start = 0;
+  if constexpr (DOC) start = p.bounds[2 * ((size_t)b * T + qc)];
+  const int lo_row = max(qc - W + 1, start);
+  const unsigned n_row = (unsigned)(qc - lo_row + 1);
+  const int wlo0 = __builtin_amdgcn_readlane(lo_row, 0);
+  const int wlo1 = __builtin_amdgcn_readlane(lo_row, 31);
+  int lo_q0 = max(q0 - W + 1, 0);   // first key any query of the workgroup sees
+  if constexpr (DOC) lo_q0 = max(lo_q0, p.bounds[2 * ((size_t)b * T + q0)]);
+  const int kt_lo = lo_q0 / BN;
   const int kt_hi = min(T - 1, q0 + BM - 1) / BN;
 
   int krow[NKS];
@@ -232,12 +243,12 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) dq_bf16_kernel(Params p) {
   __syncthreads();
   for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
     if (kt + 1 <= kt_hi) tl.load(p, kbase, vbase, K1, V1, kt + 1, tid);
-    dq_tile<D>(dqacc, qreg, oreg, K0, V0, krow, ktr1, ktr2, kt * BN, qw, myq, T, W, p.c, nl2, ndl, hi);
+    dq_tile<D>(dqacc, qreg, oreg, K0, V0, krow, ktr1, ktr2, kt * BN, qw, T, lo_row, n_row, wlo0, wlo1, p.c, nl2, ndl, hi);
     wait_vmem();
     __syncthreads();
     if (kt + 1 > kt_hi) break;
     if (kt + 2 <= kt_hi) tl.load(p, kbase, vbase, K0, V0, kt + 2, tid);
-    dq_tile<D>(dqacc, qreg, oreg, K1, V1, krow, ktr1, ktr2, (kt + 1) * BN, qw, myq, T, W, p.c, nl2, ndl, hi);
+    dq_tile<D>(dqacc, qreg, oreg, K1, V1, krow, ktr1, ktr2, (kt + 1) * BN, qw, T, lo_row, n_row, wlo0, wlo1, p.c, nl2, ndl, hi);
     wait_vmem();
     __syncthreads();
   }
@@ -260,7 +271,10 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) dq_bf16_kernel(Params p) {
 template <int D, bool GATE>
 static hipError_t launch_t(const AttnShape& a, const Params& p, hipStream_t s) {
   const unsigned blocks = (unsigned)p.nqb * a.B * a.H;
-  hipLaunchKernelGGL((dq_bf16_kernel<D, GATE>), dim3(blocks), dim3(64 * dqk::NW), 0, s, p);
+  if (a.bounds)
+    hipLaunchKernelGGL((dq_bf16_kernel<D, GATE, true>), dim3(blocks), dim3(64 * dqk::NW), 0, s, p);
+  else
+    hipLaunchKernelGGL((dq_bf16_kernel<D, GATE, false>), dim3(blocks), dim3(64 * dqk::NW), 0, s, p);
   return hipGetLastError();
 }
 
@@ -271,7 +285,7 @@ hipError_t launch_dq_bf16(const AttnShape& a, const void* q, const void* k, cons
                           const float* ndelta, void* dq, hipStream_t s) {
   dqk::Params p;
   p.q = (const bf16*)q; p.k = (const bf16*)k; p.v = (const bf16*)v; p.ve = (const bf16*)ve;
-  p.gate = gate; p.dO = (const bf16*)dO; p.nlse2 = nlse2; p.ndelta = ndelta; p.dq = (bf16*)dq;
+  p.gate = gate; p.bounds = a.bounds; p.dO = (const bf16*)dO; p.nlse2 = nlse2; p.ndelta = ndelta; p.dq = (bf16*)dq;
   p.B = a.B; p.T = a.T; p.H = a.H; p.window = a.window;
   p.nqb = (a.T + dqk::BM - 1) / dqk::BM;
   p.c = a.scale * kLog2e;

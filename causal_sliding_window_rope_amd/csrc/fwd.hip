@@ -43,6 +43,7 @@ template <int D> struct Cfg {
 
 struct Params {
   const bf16* q; const bf16* k; const bf16* v; const bf16* ve; const float* gate;
+  const int* bounds;   // per-token document [start, end) (document masking only)
   bf16* o; float* lse;
   int B, T, H, window, nqb;
   float c;      // scale * log2(e)
@@ -121,18 +122,40 @@ struct WaveState {
   float m_ref, l_run;
 };
 
+// Keys visible to this lane's query row: [lo, lo + n) (causal window, sequence end and, with
+// document masking, the start of the row's document); wlo0 / wlo1: lo of the wave's first and
+// last query (lo never decreases along a row, so these bound the whole wave).
+struct RowRange {
+  int lo;
+  unsigned n;
+  int wlo0, wlo1;
+};
+
+template <bool DOC>
+__device__ __forceinline__ RowRange row_range(const int* bounds, int b, int T, int W, int myq) {
+  const int qc = min(myq, T - 1);
+  int start = 0;
+  if constexpr (DOC) start = bounds[2 * ((size_t)b * T + qc)];
+  RowRange r;
+  r.lo = max(qc - W + 1, start);
+  r.n = (unsigned)(qc - r.lo + 1);
+  r.wlo0 = __builtin_amdgcn_readlane(r.lo, 0);
+  r.wlo1 = __builtin_amdgcn_readlane(r.lo, 31);
+  return r;
+}
+
 // One 64-key tile for one wave (32 query rows): S^T = K Q^T, mask, online softmax, O^T += V^T P^T.
 template <int D>
 __device__ __forceinline__ void tile_step(WaveState<D>& ws, const bf16x8* qreg,
                                           const lds_t<bf16>* ks, const lds_t<bf16>* vs,
                                           const int* krow, const int* vtr1, const int* vtr2,
-                                          int k0, int qw, int myq, int T, int W, float c,
+                                          int k0, int qw, int T, const RowRange& rr, float c,
                                           int lane) {
   constexpr int NKS = D / 16, NDB = D / 32;
   const int l32 = lane & 31, hi = lane >> 5;
-  const bool skip = (k0 > qw + 31) || (k0 + BN - 1 < qw - W + 1);
+  const bool skip = (k0 > qw + 31) || (k0 + BN - 1 < rr.wlo0);
   if (skip) return;
-  const bool need_mask = (k0 + BN - 1 > qw) || (k0 < qw + 31 - W + 1) || (k0 + BN > T);
+  const bool need_mask = (k0 + BN - 1 > qw) || (k0 < rr.wlo1) || (k0 + BN > T);
   // All K operands of the tile are requested before the S MFMAs and all V^T operands right
   // after them, so the LDS reads overlap one another (and the softmax arithmetic) instead of
   // each MFMA waiting for its own read.
@@ -167,9 +190,9 @@ __device__ __forceinline__ void tile_step(WaveState<D>& ws, const bf16x8* qreg,
   sched_fence();
   if (need_mask) {
     branch_keep();
-    // key k0 + t is visible iff t - lo lies in [0, n): lo, n from the row's window and T
-    const int lo = max(myq - W + 1, 0) - k0 - 4 * hi;
-    const unsigned n = (unsigned)(min(myq, T - 1) - max(myq - W + 1, 0) + 1);
+    // key k0 + t is visible iff t - lo lies in [0, n): the row's keys are [rr.lo, rr.lo + rr.n)
+    const int lo = rr.lo - k0 - 4 * hi;
+    const unsigned n = rr.n;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -232,7 +255,7 @@ __device__ __forceinline__ void tile_step(WaveState<D>& ws, const bf16x8* qreg,
     for (int sp = 0; sp < 2; ++sp) ws.oacc[db] = mfma32(va1[db][sp], pb[1][sp], ws.oacc[db]);
 }
 
-template <int D, bool GATE>
+template <int D, bool GATE, bool DOC>
 __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(Params p) {
   using C = Cfg<D>;
   constexpr int NDB = D / 32;
@@ -274,7 +297,10 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(Params p) {
     }
   }
 
-  const int kt_lo = max(0, q0 - W + 1) / BN;
+  const RowRange rr = row_range<DOC>(p.bounds, b, T, W, myq);
+  int lo_q0 = max(q0 - W + 1, 0);   // first key any query of the workgroup sees
+  if constexpr (DOC) lo_q0 = max(lo_q0, p.bounds[2 * ((size_t)b * T + q0)]);
+  const int kt_lo = lo_q0 / BN;
   const int kt_hi = min(T - 1, q0 + BM - 1) / BN;
 
   WaveState<D> ws;
@@ -309,12 +335,12 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(Params p) {
   // Two tiles per trip so that each LDS buffer is named statically.
   for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
     if (kt + 1 <= kt_hi) tl.load(p, kbase, vbase, K1, V1, kt + 1, tid);
-    tile_step<D>(ws, qreg, K0, V0, krow, vtr1, vtr2, kt * BN, qw, myq, T, W, p.c, lane);
+    tile_step<D>(ws, qreg, K0, V0, krow, vtr1, vtr2, kt * BN, qw, T, rr, p.c, lane);
     wait_vmem();
     __syncthreads();
     if (kt + 1 > kt_hi) break;
     if (kt + 2 <= kt_hi) tl.load(p, kbase, vbase, K0, V0, kt + 2, tid);
-    tile_step<D>(ws, qreg, K1, V1, krow, vtr1, vtr2, (kt + 1) * BN, qw, myq, T, W, p.c, lane);
+    tile_step<D>(ws, qreg, K1, V1, krow, vtr1, vtr2, (kt + 1) * BN, qw, T, rr, p.c, lane);
     wait_vmem();
     __syncthreads();
   }
@@ -348,6 +374,7 @@ __global__ void __launch_bounds__(64) fwd_f32_kernel(const float* __restrict__ q
                                                      const float* __restrict__ v,
                                                      const float* __restrict__ ve,
                                                      const float* __restrict__ gate,
+                                                     const int* __restrict__ bounds,
                                                      float* __restrict__ o, float* __restrict__ lse,
                                                      int T, int H, int W, float scale) {
   constexpr int PER = D / 64;
@@ -357,7 +384,8 @@ __global__ void __launch_bounds__(64) fwd_f32_kernel(const float* __restrict__ q
 #pragma unroll
   for (int e = 0; e < PER; ++e) { qv[e] = q[qrow * D + lane + 64 * e]; acc[e] = 0.f; }
   float m = -INFINITY, l = 0.f;
-  for (int j = max(0, i - W + 1); j <= i; ++j) {
+  const int j0 = max(max(0, i - W + 1), bounds ? bounds[2 * ((size_t)b * T + i)] : 0);
+  for (int j = j0; j <= i; ++j) {
     const size_t krow = ((size_t)b * T + j) * H + h;
     float d = 0.f;
 #pragma unroll
@@ -389,12 +417,17 @@ static hipError_t launch_fwd_bf16_t(const AttnShape& a, const void* q, const voi
                                     hipStream_t s) {
   fwdk::Params p;
   p.q = (const bf16*)q; p.k = (const bf16*)k; p.v = (const bf16*)v; p.ve = (const bf16*)ve;
-  p.gate = gate; p.o = (bf16*)o; p.lse = lse;
+  p.gate = gate; p.bounds = a.bounds; p.o = (bf16*)o; p.lse = lse;
   p.B = a.B; p.T = a.T; p.H = a.H; p.window = a.window;
   p.nqb = (a.T + fwdk::BM - 1) / fwdk::BM;
   p.c = a.scale * kLog2e;
   const unsigned blocks = (unsigned)p.nqb * a.B * a.H;
-  hipLaunchKernelGGL((fwdk::fwd_bf16_kernel<D, GATE>), dim3(blocks), dim3(64 * fwdk::NW), 0, s, p);
+  if (a.bounds)
+    hipLaunchKernelGGL((fwdk::fwd_bf16_kernel<D, GATE, true>), dim3(blocks), dim3(64 * fwdk::NW), 0,
+                       s, p);
+  else
+    hipLaunchKernelGGL((fwdk::fwd_bf16_kernel<D, GATE, false>), dim3(blocks), dim3(64 * fwdk::NW), 0,
+                       s, p);
   return hipGetLastError();
 }
 
@@ -412,11 +445,11 @@ hipError_t launch_fwd(const AttnShape& a, const void* q, const void* k, const vo
   dim3 grid(a.T, a.B * a.H);
   if (a.D == 64)
     hipLaunchKernelGGL(fwd_f32_kernel<64>, grid, dim3(64), 0, s, (const float*)q, (const float*)k,
-                       (const float*)v, (const float*)ve, gate, (float*)o, lse, a.T, a.H, a.window,
+                       (const float*)v, (const float*)ve, gate, a.bounds, (float*)o, lse, a.T, a.H, a.window,
                        a.scale);
   else
     hipLaunchKernelGGL(fwd_f32_kernel<128>, grid, dim3(64), 0, s, (const float*)q, (const float*)k,
-                       (const float*)v, (const float*)ve, gate, (float*)o, lse, a.T, a.H, a.window,
+                       (const float*)v, (const float*)ve, gate, a.bounds, (float*)o, lse, a.T, a.H, a.window,
                        a.scale);
   return hipGetLastError();
 }

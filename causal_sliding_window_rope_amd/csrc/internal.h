@@ -10,7 +10,10 @@ struct AttnShape {
   int B, T, H, D;
   int window;   // already clamped: 1 <= window <= T
   float scale;
+  const int* bounds = nullptr;   // optional per-token document [start, end), (B, T, 2) int32
 };
+
+hipError_t launch_doc_bounds(const int* doc_id, int* bounds, int B, int T, hipStream_t s);
 
 hipError_t launch_rope_table(float* cos_sin, int T, int D, double base, hipStream_t s);
 hipError_t launch_rope_qknorm_fwd(const void* q, const void* k, const float* cs, void* qn, void* kn,

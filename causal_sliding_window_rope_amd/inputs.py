@@ -12,6 +12,10 @@ Recipe (the same on every machine):
   workloads the stream continues with x (B, T, C), Wg (32, H) scaled by 0.02
   (standard deviation 0.02), the embedding table (vocab, H*D), then token ids
   ``integers(0, vocab, (B, T))``; ve = table[ids];
+* document-masked workloads continue with the document layout: per row,
+  documents of length max(1, round(lognormal(log(mean) - 1/2, 1))) tokens
+  back to back, the last one cut at the row end (a BOS-aligned packed row);
+  doc_id (B, T) int32 numbers the documents of a row 0, 1, ...;
 * cast float64 -> float32 (numpy, round to nearest even), then for bf16
   workloads float32 -> bfloat16 with round-to-nearest-even on the bit pattern.
   bf16 values are returned as float32 arrays whose values are exactly
@@ -52,6 +56,7 @@ class Workload:
     gate: bool = False   # gated value embedding on V
     C: int = 0           # width of the block input x (gate workloads only)
     vocab: int = VOCAB
+    doc_mean: int = 0    # mean document length of a packed row (0: one document per row)
 
     @property
     def scale(self) -> float:
@@ -68,6 +73,9 @@ WORKLOADS = {
     "d24_full": Workload("d24_full", B=16, T=2048, H=12, D=128, window=2048, dtype="bf16", seed=1003),
     "d24_short_ve": Workload("d24_short_ve", B=16, T=2048, H=12, D=128, window=1024, dtype="bf16",
                              seed=5, gate=True, C=1536),
+    # the d24 short layer on BOS-aligned rows packing documents of ~512 tokens on average
+    "d24_short_doc": Workload("d24_short_doc", B=16, T=2048, H=12, D=128, window=1024,
+                              dtype="bf16", seed=7, doc_mean=512),
 }
 
 
@@ -105,6 +113,8 @@ def make_inputs(wl: Workload, heads: tuple[int, int] | None = None) -> dict[str,
         out["ve"] = table[ids]
         out["ids"] = ids
         del table
+    if wl.doc_mean > 0:
+        out["doc_id"] = doc_layout(rng, wl.B, wl.T, wl.doc_mean)
     if wl.dtype == "bf16":
         for name in ("q", "k", "v", "dO", "x"):
             if name in out:
@@ -119,11 +129,27 @@ def make_inputs(wl: Workload, heads: tuple[int, int] | None = None) -> dict[str,
             out["ve"] = np.ascontiguousarray(out["ve"][:nb].reshape(nb, wl.T, wl.H, wl.D)[:, :, :nh]
                                              .reshape(nb, wl.T, nh * wl.D))
             out["ids"] = out["ids"][:nb]
+        if wl.doc_mean > 0:
+            out["doc_id"] = np.ascontiguousarray(out["doc_id"][:nb])
     return out
 
 
+def doc_layout(rng, B: int, T: int, mean_len: float) -> np.ndarray:
+    """(B, T) int32 document numbers of BOS-aligned packed rows (see the module recipe)."""
+    ids = np.zeros((B, T), dtype=np.int32)
+    for b in range(B):
+        t, d = 0, 0
+        while t < T:
+            n = max(1, int(round(rng.lognormal(np.log(mean_len) - 0.5, 1.0))))
+            ids[b, t:t + n] = d
+            t += n
+            d += 1
+    return ids
+
+
 def small_workload(B: int, T: int, H: int, D: int, window: int, dtype: str, seed: int,
-                   gate: bool = False, C: int = 64) -> Workload:
+                   gate: bool = False, C: int = 64, doc_mean: int = 0) -> Workload:
     """A parity-test case with arbitrary (small) sizes and the same recipe."""
     return Workload(f"case_B{B}_T{T}_H{H}_D{D}_W{window}_{dtype}", B=B, T=T, H=H, D=D,
-                    window=window, dtype=dtype, seed=seed, gate=gate, C=C if gate else 0)
+                    window=window, dtype=dtype, seed=seed, gate=gate, C=C if gate else 0,
+                    doc_mean=doc_mean)

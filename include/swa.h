@@ -127,17 +127,29 @@ int ve_gate_v_bwd(const void* x, int ldx, const float* Wg, const float* gate,
                   swa_dtype dtype, void* stream);
 
 /*
+ * swa_doc_bounds — document segments of packed rows ("从4万美元到73美元" §6.1: BOS-aligned rows
+ *   hold several documents; per-document attention is the variable-length attention its list of
+ *   tried ideas names). A document is a maximal run of equal ids along a row; for each token
+ *   the call writes doc_bounds[(b*T + t)*2 + 0] = first position of its run and [... + 1] = one
+ *   past the last. Computed once per batch; every attention call of the step can reuse it.
+ *   doc_id: device (B,T) int32, read.   doc_bounds: device (B,T,2) int32, written.
+ */
+int swa_doc_bounds(const int* doc_id, int* doc_bounds, int B, int T, void* stream);
+
+/*
  * swa_fwd — causal sliding-window attention forward ("GPT-2 124M 复现" §3, §19).
  *   s_ij = scale * q_i . k_j for max(0, i-W+1) <= j <= i; lse_i = log sum_j exp(s_ij);
  *   O_i = sum_j exp(s_ij - lse_i) v_eff_j, v_eff = v (+ gate * ve when ve and gate are given).
  *   q, k, v: device (B,T,H,D) dtype (normally qn, kn from rope_qknorm_fwd), read.
  *   ve, gate: both NULL, or ve (B,T,H*D) dtype and gate (B,T,H) float, read.
  *   o  : device (B,T,H,D) dtype, written.     lse: device (B,H,T) float, natural log, written.
+ *   doc_bounds: NULL, or swa_doc_bounds' output for this batch: then a token also sees only
+ *   keys of its own document (j >= start of i's run), on top of the causal window.
  *   scale: finite, > 0 (1/sqrt(D) for this model).
  */
 int swa_fwd(const void* q, const void* k, const void* v, const void* ve, const float* gate,
-            void* o, float* lse, int B, int T, int H, int D, int window, float scale,
-            swa_dtype dtype, void* stream);
+            const int* doc_bounds, void* o, float* lse, int B, int T, int H, int D, int window,
+            float scale, swa_dtype dtype, void* stream);
 
 /* Bytes of workspace swa_bwd needs: the row terms -delta and -lse*log2(e), each (B,H,T) float32,
  * 256-byte aligned inside the block and followed by 512 bytes of slack. */
@@ -148,16 +160,17 @@ size_t swa_bwd_workspace_size(int B, int T, int H, int D, swa_dtype dtype);
  *   P = exp(s - lse); dv_eff = P^T dO; dP = dO v_eff^T; delta_i = dO_i . O_i;
  *   dS = P * (dP - delta); dq = scale dS k; dk = scale dS^T q. Outputs are bitwise repeatable.
  *   With the gate: dv = dv_eff, dve = gate * dv_eff, dgate = sum_d dv_eff * ve.
- *   q, k, v, ve, gate: as given to swa_fwd.  o, lse: swa_fwd's outputs.  dO: (B,T,H,D) dtype.
+ *   q, k, v, ve, gate, doc_bounds: as given to swa_fwd.  o, lse: swa_fwd's outputs.
+ *   dO: (B,T,H,D) dtype.
  *   dq, dk, dv: device (B,T,H,D) dtype, written.
  *   dve (B,T,H*D) dtype and dgate (B,T,H) float: written when the gate is used (both
  *   required then), must be NULL otherwise.
  *   workspace: device, >= swa_bwd_workspace_size() bytes, 256-byte aligned, clobbered.
  */
 int swa_bwd(const void* q, const void* k, const void* v, const void* ve, const float* gate,
-            const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
-            void* dve, float* dgate, void* workspace, size_t ws_bytes, int B, int T, int H,
-            int D, int window, float scale, swa_dtype dtype, void* stream);
+            const int* doc_bounds, const void* o, const float* lse, const void* dO, void* dq,
+            void* dk, void* dv, void* dve, float* dgate, void* workspace, size_t ws_bytes, int B,
+            int T, int H, int D, int window, float scale, swa_dtype dtype, void* stream);
 
 /*
  * The three stages swa_bwd runs, for callers that schedule or time them separately. Call them
@@ -175,9 +188,9 @@ int swa_bwd_preprocess(const void* o, const void* dO, const float* lse, void* wo
  *   filled by swa_bwd_preprocess.
  */
 int swa_bwd_dkdv(const void* q, const void* k, const void* v, const void* ve, const float* gate,
-                 const float* lse, const void* dO, void* dk, void* dv, void* dve, float* dgate,
-                 void* workspace, size_t ws_bytes, int B, int T, int H, int D, int window,
-                 float scale, swa_dtype dtype, void* stream);
+                 const int* doc_bounds, const float* lse, const void* dO, void* dk, void* dv,
+                 void* dve, float* dgate, void* workspace, size_t ws_bytes, int B, int T, int H,
+                 int D, int window, float scale, swa_dtype dtype, void* stream);
 
 /*
  * swa_bwd_dq — the query-block-major part: recomputes the scores per query block and writes
@@ -185,8 +198,9 @@ int swa_bwd_dkdv(const void* q, const void* k, const void* v, const void* ve, co
  *   swa_bwd_preprocess. May run before, after or concurrently with swa_bwd_dkdv.
  */
 int swa_bwd_dq(const void* q, const void* k, const void* v, const void* ve, const float* gate,
-               const float* lse, const void* dO, void* dq, void* workspace, size_t ws_bytes, int B,
-               int T, int H, int D, int window, float scale, swa_dtype dtype, void* stream);
+               const int* doc_bounds, const float* lse, const void* dO, void* dq, void* workspace,
+               size_t ws_bytes, int B, int T, int H, int D, int window, float scale,
+               swa_dtype dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -81,8 +81,13 @@ def gpu_layer(x: dict, wl, window: int):
         ve = dev(x["ve"], dt)
         gate = sw.ve_gate_v(xg, Wg)
         out["gate"] = gate
-    o, lse = sw.swa_fwd(qn, kn, v, window, wl.scale, ve=ve, gate=gate)
-    grads = sw.swa_bwd(qn, kn, v, o, lse, dO, window, wl.scale, ve=ve, gate=gate)
+    bounds = None
+    if "doc_id" in x:
+        bounds = sw.swa_doc_bounds(torch.from_numpy(x["doc_id"].astype(np.int32)).cuda())
+        out["doc_bounds"] = bounds
+    o, lse = sw.swa_fwd(qn, kn, v, window, wl.scale, ve=ve, gate=gate, doc_bounds=bounds)
+    grads = sw.swa_bwd(qn, kn, v, o, lse, dO, window, wl.scale, ve=ve, gate=gate,
+                       doc_bounds=bounds)
     dqn, dkn, dv = grads[:3]
     dq, dk = sw.rope_qknorm_bwd(q, k, cs, dqn, dkn, wl.eps)
     out.update(O=o, lse=lse, dqh=dqn, dkh=dkn, dv=dv, dq=dq, dk=dk)
@@ -103,16 +108,18 @@ def oracle_layer(x: dict, wl, window: int, sel=None):
         B, T = wl.B, wl.T
         gk = dict(x32=x["x"][..., :32].astype(np.float64), Wg=x["Wg"].astype(np.float64),
                   ve=x["ve"].astype(np.float64))
+    doc = x.get("doc_id")
     if sel is not None:
         b, h = sel
         f = {n: a[b:b + 1, :, h:h + 1] for n, a in f.items()}
+        doc = doc[b:b + 1] if doc is not None else None
         if wl.gate:
             D = wl.D
             gk = dict(x32=gk["x32"][b:b + 1], Wg=gk["Wg"][:, h:h + 1],
                       ve=gk["ve"][b:b + 1, :, h * D:(h + 1) * D])
     fwd = oracle.layer_fwd(f["q"], f["k"], f["v"], window, round_boundary=(wl.dtype == "bf16"),
-                           **kw, **gk)
-    bwd = oracle.layer_bwd(f["q"], f["k"], f["v"], f["dO"], window, fwd, **kw, **gk)
+                           doc_id=doc, **kw, **gk)
+    bwd = oracle.layer_bwd(f["q"], f["k"], f["v"], f["dO"], window, fwd, doc_id=doc, **kw, **gk)
     return fwd, bwd
 
 

@@ -52,8 +52,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def _fwd(lib, q=P, k=P, v=P, ve=None, gate=None, o=P, lse=P, B=1, T=8, H=1, D=64, W=4, scale=0.125,
-         dt=1):
-    return lib.swa_fwd(q, k, v, ve, gate, o, lse, B, T, H, D, W, scale, dt, None)
+         dt=1, doc=None):
+    return lib.swa_fwd(q, k, v, ve, gate, doc, o, lse, B, T, H, D, W, scale, dt, None)
 
 
 def test_swa_fwd_validation(lib):
@@ -71,6 +71,15 @@ def test_swa_fwd_validation(lib):
     assert _fwd(lib, ve=P) == INVALID          # ve without gate
     assert _fwd(lib, gate=P) == INVALID        # gate without ve
     assert _fwd(lib, B=1 << 20, T=1 << 12, H=1 << 4, D=128) == UNSUPPORTED
+    assert _fwd(lib, doc=MIS) == ALIGN                     # document bounds misaligned
+
+
+def test_doc_bounds_validation(lib):
+    assert lib.swa_doc_bounds(None, P, 2, 8, None) == INVALID
+    assert lib.swa_doc_bounds(P, None, 2, 8, None) == INVALID
+    assert lib.swa_doc_bounds(P, ctypes.c_void_p(0x20000), 0, 8, None) == INVALID
+    assert lib.swa_doc_bounds(P, P, 2, 8, None) == INVALID       # output aliases the ids
+    assert lib.swa_doc_bounds(P, ctypes.c_void_p(0x20008), 2, 8, None) == ALIGN
 
 
 def test_swa_bwd_validation(lib):
@@ -79,7 +88,7 @@ def test_swa_bwd_validation(lib):
     assert lib.swa_bwd_workspace_size(2, 64, 3, 96, 1) == 0
 
     def bwd(ws=P, ws_bytes=ws_need, ve=None, gate=None, dve=None, dgate=None, W=8, dO=P):
-        return lib.swa_bwd(P, P, P, ve, gate, P, P, dO, P, P, P, dve, dgate, ws, ws_bytes, 2, 64, 3,
+        return lib.swa_bwd(P, P, P, ve, gate, None, P, P, dO, P, P, P, dve, dgate, ws, ws_bytes, 2, 64, 3,
                            64, W, 0.125, 1, None)
 
     assert bwd(ws=None) == WORKSPACE
@@ -92,11 +101,11 @@ def test_swa_bwd_validation(lib):
 
     # the two compute stages check the same arguments
     def dkdv(ws=P, ws_bytes=ws_need, W=8):
-        return lib.swa_bwd_dkdv(P, P, P, None, None, P, P, P, P, None, None, ws, ws_bytes, 2, 64, 3,
+        return lib.swa_bwd_dkdv(P, P, P, None, None, None, P, P, P, P, None, None, ws, ws_bytes, 2, 64, 3,
                                 64, W, 0.125, 1, None)
 
     def dq(ws=P, ws_bytes=ws_need, W=8, ve=None, gate=None):
-        return lib.swa_bwd_dq(P, P, P, ve, gate, P, P, P, ws, ws_bytes, 2, 64, 3, 64, W, 0.125, 1,
+        return lib.swa_bwd_dq(P, P, P, ve, gate, None, P, P, P, ws, ws_bytes, 2, 64, 3, 64, W, 0.125, 1,
                               None)
 
     assert dkdv(ws=None) == WORKSPACE and dq(ws=None) == WORKSPACE
