@@ -278,6 +278,91 @@ def kernel_sources_sha256(kernel: str) -> str:
     return h.hexdigest()
 
 
+DECODE_METRIC = "decode tokens/s (one new token per sequence through 24 sliding-window layers)"
+
+
+def run_decode_bench(args):
+    """Sliding-window decoding from a K/V cache: B = 32 sequences at position 2047 (full
+    context) through the 24 d24 layers (windows 3-short:1-long), ring caches of 2048 slots per
+    layer filled with synthetic N(0, 1) keys / values. One step = every layer's positional
+    prologue (RoPE + QK-norm of the new q, k; k, v stored in the cache) and its windowed
+    attention over the cache; tokens per step = B. The attention reads W cached K and V rows per
+    (sequence, head), so it is priced against HBM bandwidth."""
+    import torch
+    from causal_sliding_window_rope_amd import binding as sw
+    from causal_sliding_window_rope_amd.inputs import sssl_windows
+    lib = sw.load()
+    B, H, D, cap, p_pos = 32, 12, 128, 2048, 2047
+    windows = sssl_windows(24, 1024, 2048)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4242)
+    rnd = lambda *shape: torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16)
+    layers = []
+    for W in windows:
+        layers.append(dict(W=W, q=rnd(B, H, D), k=rnd(B, H, D), v=rnd(B, H, D),
+                           kc=rnd(B, cap, H, D), vc=rnd(B, cap, H, D),
+                           qn=torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda"),
+                           o=torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda"),
+                           lse=torch.empty((B, H), dtype=torch.float32, device="cuda")))
+    cs = sw.rope_table(cap, D, 10000.0)
+    pos = torch.full((B,), p_pos, dtype=torch.int32, device="cuda")
+    nws = max(sw.swa_decode_workspace_size(B, H, D, cap, max(windows)), 256)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    P, stream = sw._ptr, sw._stream()
+    scale = D ** -0.5
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def call(name, *a):
+        st = getattr(lib, name)(*a)
+        if st != 0:
+            raise sw.SwaError(name, st, lib.swa_last_error().decode())
+
+    def step(rec):
+        for li, t in enumerate(layers):
+            call("swa_decode_prologue", P(t["q"]), P(t["k"]), P(t["v"]), P(cs), cap, P(pos),
+                 P(t["qn"]), P(t["kc"]), P(t["vc"]), B, H, D, cap, 1e-6, sw.SWA_BF16, stream)
+            if rec: rec[li][0].record()
+            call("swa_decode", P(t["qn"]), P(t["kc"]), P(t["vc"]), P(pos), P(t["o"]), P(t["lse"]),
+                 P(ws), nws, B, H, D, cap, t["W"], scale, sw.SWA_BF16, stream)
+            if rec: rec[li][1].record()
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    recs = [[[ev(), ev()] for _ in layers] for _ in range(args.steps)]
+    e0, e1 = ev(), ev()
+    e0.record()
+    for k in range(args.steps):
+        step(recs[k])
+    e1.record()
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / args.steps
+    dec_ms = sum(r[l][0].elapsed_time(r[l][1]) for r in recs for l in range(len(layers)))
+    launches = args.steps * len(layers)
+    # algorithmic HBM bytes of the attention: W cached K and V rows per (sequence, head), the
+    # query read and the output written (bf16), lse (fp32)
+    def attn_bytes(W):
+        return B * H * (2 * W * D * 2 + 2 * D * 2 + 4)
+    total_bytes = sum(attn_bytes(l["W"]) for l in layers)
+    achieved = total_bytes / (dec_ms / args.steps * 1e-3) / 1e9
+    return {
+        "metric": DECODE_METRIC, "value": round(B / (step_ms * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "d24 decoding: 24 layers (18 x window 1024, 6 x 2048), 32 "
+                               "sequences at position 2047, ring caches of 2048 slots, H=12, D=128",
+                   "batch": B, "context": p_pos + 1, "parallelism": "single GPU"},
+        "breakdown": {"swa_decode_ms_per_step": round(dec_ms / args.steps, 4),
+                      "prologue_ms_per_step": round(step_ms - dec_ms / args.steps, 4),
+                      "attention_bytes_per_step": total_bytes},
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel + combine_kernel (swa_decode)",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "avg_launch_us": round(dec_ms / launches * 1e3, 2), "traffic": None},
+    }
+
+
 def traffic_from_profile(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
     (FETCH_SIZE and WRITE_SIZE, each scaled by its copy-kernel calibration factor), if the
@@ -338,6 +423,38 @@ def cpu_baseline(args):
                       f"{platform.processor() or platform.machine()}"}
 
 
+def cpu_baseline_decode(args):
+    """The decoding oracle (float64 numpy) on whole sequences of the decode workload: the
+    positional prologue and the windowed attention of one new token, sequences until about
+    args.cpu_seconds; tokens/s scaled to one token through all 24 layers."""
+    import numpy as np
+    from oracle.decode import decode_fwd, rope_qknorm_at
+    from causal_sliding_window_rope_amd.inputs import sssl_windows
+    H, D, cap, p_pos = 12, 128, 2048, 2047
+    windows = sssl_windows(24, 1024, 2048)
+    rng = np.random.default_rng(4242)
+    kc = rng.standard_normal((1, cap, H, D))
+    vc = rng.standard_normal((1, cap, H, D))
+    secs, layers_done = 0.0, 0
+    while secs < args.cpu_seconds and layers_done < 2400:
+        W = windows[layers_done % len(windows)]
+        q = rng.standard_normal((1, H, D))
+        t0 = time.perf_counter()
+        qn = rope_qknorm_at(q, np.array([p_pos]), 10000.0, 1e-6)
+        decode_fwd(qn, kc, vc, np.array([p_pos]), W, D ** -0.5)
+        secs += time.perf_counter() - t0
+        layers_done += 1
+    tokens = layers_done / len(windows)
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    return {"value": round(tokens / secs, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 numpy decoding oracle, {layers_done} layer steps of one sequence "
+                      f"({tokens:.1f} tokens through 24 layers) in {secs:.1f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -345,7 +462,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="sssl24",
                     choices=["sssl24", "d24_short", "d24_full", "gpt2_124m", "d24_short_ve",
-                             "d24_short_doc"])
+                             "d24_short_doc", "d24_decode"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
@@ -367,6 +484,12 @@ def main():
         print(f"bench.py: --gpus {args.gpus} is not supported; this build measures one GPU "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "d24_decode":
+        res = run_decode_bench(args)
+        if not args.no_cpu_baseline:
+            res["cpu_baseline"] = cpu_baseline_decode(args)
+        print(json.dumps(res), flush=True)
+        return
     res = run_bench(args)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args)

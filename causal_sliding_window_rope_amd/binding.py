@@ -42,6 +42,9 @@ SIGNATURES = {
                           _I, _I, _I, _I, _I, _F, _I, _P]),
     "swa_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _F, _I,
                         _P]),
+    "swa_decode_prologue": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
+    "swa_decode_workspace_size": (_S, [_I, _I, _I, _I, _I]),
+    "swa_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _F, _I, _P]),
 }
 
 _lib = None
@@ -251,3 +254,45 @@ def swa_bwd_stages(q, k, v, o, lse, dO, window: int, scale: float | None = None,
     if ve is not None:
         return dq, dk, dv, dve, dgate
     return dq, dk, dv
+
+
+def swa_decode_prologue(q, k, v, cos_sin, pos, k_cache, v_cache, eps: float = 1e-6, qn=None):
+    """RoPE at pos[b] + QK-norm of one new token per sequence; stores k, v in the ring caches.
+    q, k, v: (B, H, D); caches: (B, cap, H, D); pos: (B,) int32. Returns qn (B, H, D)."""
+    B, H, D = q.shape
+    cap = k_cache.shape[1]
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, (B, H, D), q.dtype)
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _check(t, n, (B, cap, H, D), q.dtype)
+    _check(pos, "pos", (B,), torch.int32)
+    _check(cos_sin, "cos_sin", (cos_sin.shape[0], D // 2, 2), torch.float32)
+    qn = torch.empty_like(q) if qn is None else qn
+    _call("swa_decode_prologue", _ptr(q), _ptr(k), _ptr(v), _ptr(cos_sin), cos_sin.shape[0],
+          _ptr(pos), _ptr(qn), _ptr(k_cache), _ptr(v_cache), B, H, D, cap, float(eps), _dt(q),
+          _stream())
+    return qn
+
+
+def swa_decode_workspace_size(B: int, H: int, D: int, cap: int, window: int) -> int:
+    return load().swa_decode_workspace_size(B, H, D, cap, int(window))
+
+
+def swa_decode(qn, k_cache, v_cache, pos, window: int, scale: float | None = None,
+               workspace=None, out=None, lse=None):
+    """Attention of each sequence's new query over its cached window. Returns (o, lse)."""
+    B, H, D = qn.shape
+    cap = k_cache.shape[1]
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _check(t, n, (B, cap, H, D), qn.dtype)
+    _check(pos, "pos", (B,), torch.int32)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if workspace is None:
+        n = swa_decode_workspace_size(B, H, D, cap, window)
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=qn.device)
+    o = torch.empty_like(qn) if out is None else out
+    lse = torch.empty((B, H), dtype=torch.float32, device=qn.device) if lse is None else lse
+    _call("swa_decode", _ptr(qn), _ptr(k_cache), _ptr(v_cache), _ptr(pos), _ptr(o), _ptr(lse),
+          _ptr(workspace), workspace.numel() * workspace.element_size(), B, H, D, cap, int(window),
+          float(scale), _dt(qn), _stream())
+    return o, lse

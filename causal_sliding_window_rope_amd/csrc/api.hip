@@ -277,4 +277,73 @@ int swa_bwd_dq(const void* q, const void* k, const void* v, const void* ve, cons
                                        dtype == SWA_BF16, (hipStream_t)stream), fn);
 }
 
+// ---- sliding-window decoding from a ring K/V cache
+
+static int check_decode_shape(const char* fn, int B, int H, int D, int cap, int dtype) {
+  if (B < 1 || H < 1 || cap < 1)
+    return fail(SWA_ERR_INVALID_ARG, "%s: B, H and the cache capacity must be >= 1", fn);
+  if (dtype != SWA_F32 && dtype != SWA_BF16)
+    return fail(SWA_ERR_INVALID_ARG, "%s: dtype must be SWA_F32 or SWA_BF16 (got %d)", fn, dtype);
+  if (D != 64 && D != 128)
+    return fail(SWA_ERR_UNSUPPORTED, "%s: head dim D must be 64 or 128 (got %d)", fn, D);
+  if ((long long)B * cap * H * D >= (1LL << 40) || (long long)B * H >= (1LL << 24))
+    return fail(SWA_ERR_UNSUPPORTED, "%s: sizes exceed the supported range", fn);
+  return 0;
+}
+
+static int decode_window(const char* fn, int window, int cap, int* w_out) {
+  if (window == SWA_WINDOW_FULL) window = cap;
+  if (window < 1 || window > cap)
+    return fail(SWA_ERR_INVALID_ARG,
+                "%s: window must be in [1, cache capacity %d] or SWA_WINDOW_FULL (got %d)", fn,
+                cap, window);
+  *w_out = window;
+  return 0;
+}
+
+int swa_decode_prologue(const void* q, const void* k, const void* v, const float* cos_sin,
+                        int table_rows, const int* pos, void* qn, void* k_cache, void* v_cache,
+                        int B, int H, int D, int cap, float eps, swa_dtype dtype, void* stream) {
+  const char* fn = "swa_decode_prologue";
+  SWA_TRY(check_decode_shape(fn, B, H, D, cap, dtype));
+  SWA_TRY(need(fn, "q", q)); SWA_TRY(need(fn, "k", k)); SWA_TRY(need(fn, "v", v));
+  SWA_TRY(need(fn, "cos_sin", cos_sin)); SWA_TRY(need(fn, "pos", pos)); SWA_TRY(need(fn, "qn", qn));
+  SWA_TRY(need(fn, "k_cache", k_cache)); SWA_TRY(need(fn, "v_cache", v_cache));
+  if (table_rows < 1) return fail(SWA_ERR_INVALID_ARG, "%s: table_rows must be >= 1", fn);
+  if (!(std::isfinite(eps) && eps >= 0.f))
+    return fail(SWA_ERR_INVALID_ARG, "%s: eps must be finite and >= 0", fn);
+  return hip_status(swa::launch_decode_prologue(q, k, v, cos_sin, table_rows, pos, qn, k_cache,
+                                                v_cache, B, H, D, cap, eps, dtype == SWA_BF16,
+                                                (hipStream_t)stream), fn);
+}
+
+size_t swa_decode_workspace_size(int B, int H, int D, int cap, int window) {
+  if (B < 1 || H < 1 || cap < 1 || (D != 64 && D != 128)) return 0;
+  if (window == SWA_WINDOW_FULL) window = cap;
+  if (window < 1 || window > cap) return 0;
+  return swa::decode_workspace_bytes(B, H, D, window);
+}
+
+int swa_decode(const void* qn, const void* k_cache, const void* v_cache, const int* pos, void* o,
+               float* lse, void* workspace, size_t ws_bytes, int B, int H, int D, int cap,
+               int window, float scale, swa_dtype dtype, void* stream) {
+  const char* fn = "swa_decode";
+  SWA_TRY(check_decode_shape(fn, B, H, D, cap, dtype));
+  SWA_TRY(need(fn, "qn", qn)); SWA_TRY(need(fn, "k_cache", k_cache));
+  SWA_TRY(need(fn, "v_cache", v_cache)); SWA_TRY(need(fn, "pos", pos));
+  SWA_TRY(need(fn, "o", o)); SWA_TRY(need(fn, "lse", lse));
+  int w = 0;
+  SWA_TRY(decode_window(fn, window, cap, &w));
+  if (!(std::isfinite(scale) && scale > 0.f))
+    return fail(SWA_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
+  const size_t need_ws = swa::decode_workspace_bytes(B, H, D, w);
+  if (!workspace || ws_bytes < need_ws)
+    return fail(SWA_ERR_WORKSPACE, "%s: workspace of %zu bytes required (got %zu)", fn, need_ws,
+                workspace ? ws_bytes : (size_t)0);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(SWA_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+  return hip_status(swa::launch_decode(qn, k_cache, v_cache, pos, o, lse, workspace, B, H, D, cap,
+                                       w, scale, dtype == SWA_BF16, (hipStream_t)stream), fn);
+}
+
 }  // extern "C"

@@ -49,4 +49,14 @@ hipError_t launch_dq_bf16(const AttnShape& a, const void* q, const void* k, cons
                           const void* ve, const float* gate, const void* dO, const float* nlse2,
                           const float* ndelta, void* dq, hipStream_t s);
 
+// Sliding-window decoding from a ring K/V cache (one new token per sequence).
+int decode_splits(int B, int H, int window);
+size_t decode_workspace_bytes(int B, int H, int D, int window);
+hipError_t launch_decode_prologue(const void* q, const void* k, const void* v, const float* cs,
+                                  int rows, const int* pos, void* qn, void* kc, void* vc, int B,
+                                  int H, int D, int cap, float eps, bool bf16, hipStream_t s);
+hipError_t launch_decode(const void* qn, const void* kc, const void* vc, const int* pos, void* o,
+                         float* lse, void* ws, int B, int H, int D, int cap, int window,
+                         float scale, bool bf16, hipStream_t s);
+
 }  // namespace swa

@@ -202,6 +202,42 @@ int swa_bwd_dq(const void* q, const void* k, const void* v, const void* ve, cons
                size_t ws_bytes, int B, int T, int H, int D, int window, float scale,
                swa_dtype dtype, void* stream);
 
+/*
+ * Sliding-window decoding from a K/V cache ("GPT-2 124M 复现" §7: generation that keeps the
+ * past keys and values instead of recomputing every prefix position). One new token per
+ * sequence b at position pos[b] >= 0; a decoding step computes row pos[b] of the training
+ * forward. The cache of a sequence is a ring of `cap` slots in the native layout
+ * (B, cap, H, D): position j lives in slot j mod cap, so cap >= the longest context means no
+ * wrap, and cap >= window suffices for a sliding window.
+ */
+
+/*
+ * swa_decode_prologue — RoPE at angle pos[b] * theta_i and the RMS QK-norm of the new q and k
+ *   (as rope_qknorm_fwd at row pos[b]); writes qn and stores the normalised k and the raw v in
+ *   slot pos[b] mod cap of the caches.
+ *   q, k, v: device (B,H,D) dtype, read.   qn: device (B,H,D) dtype, written.
+ *   cos_sin: rope_table(table_rows, D) output; positions outside [0, table_rows) give NaN in qn
+ *   and leave the caches untouched.   pos: device (B) int32, read.
+ *   k_cache, v_cache: device (B,cap,H,D) dtype, one slot per sequence written.
+ */
+int swa_decode_prologue(const void* q, const void* k, const void* v, const float* cos_sin,
+                        int table_rows, const int* pos, void* qn, void* k_cache, void* v_cache,
+                        int B, int H, int D, int cap, float eps, swa_dtype dtype, void* stream);
+
+/* Bytes of workspace swa_decode needs for these sizes (0 for invalid arguments). */
+size_t swa_decode_workspace_size(int B, int H, int D, int cap, int window);
+
+/*
+ * swa_decode — the new query of each sequence attends to positions max(0, p-W+1) .. p of its
+ *   cache (p = pos[b]); o (B,H,D) dtype and lse (B,H) float (natural log) are written.
+ *   window: 1 <= W <= cap, or SWA_WINDOW_FULL (= cap).   scale: finite, > 0.
+ *   pos[b] < 0 gives NaN for that sequence. workspace: >= swa_decode_workspace_size() bytes,
+ *   256-byte aligned, clobbered.
+ */
+int swa_decode(const void* qn, const void* k_cache, const void* v_cache, const int* pos, void* o,
+               float* lse, void* workspace, size_t ws_bytes, int B, int H, int D, int cap,
+               int window, float scale, swa_dtype dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -135,3 +135,23 @@ def test_binding_refuses_cpu_tensors(lib):
     x = torch.zeros(1, 8, 1, 64)
     with pytest.raises(ValueError):
         binding.swa_fwd(x, x, x, window=4)
+
+
+def test_decode_validation(lib):
+    ws = lib.swa_decode_workspace_size(2, 3, 64, 16, 8)
+    assert ws >= 256
+    assert lib.swa_decode_workspace_size(2, 3, 64, 16, 17) == 0      # window larger than the ring
+    assert lib.swa_decode_workspace_size(2, 3, 96, 16, 8) == 0
+
+    def dec(W=8, cap=16, wsp=P, nbytes=ws, D=64, pos=P):
+        return lib.swa_decode(P, P, P, pos, P, P, wsp, nbytes, 2, 3, D, cap, W, 0.125, 1, None)
+
+    assert dec(W=17) == INVALID
+    assert dec(W=0) == INVALID
+    assert dec(D=96) == UNSUPPORTED
+    assert dec(pos=None) == INVALID
+    assert dec(wsp=None) == WORKSPACE
+    assert dec(nbytes=ws - 1) == WORKSPACE
+    assert dec(wsp=ctypes.c_void_p(0x10010)) == ALIGN
+    assert lib.swa_decode_prologue(P, P, P, P, 0, P, P, P, P, 2, 3, 64, 16, 1e-6, 1, None) == INVALID
+    assert lib.swa_decode_prologue(P, P, P, P, 8, P, P, P, P, 2, 3, 64, 0, 1e-6, 1, None) == INVALID
