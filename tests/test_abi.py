@@ -51,6 +51,39 @@ def test_library_exports_every_declared_symbol(lib):
     assert set(binding.SIGNATURES) == set(declared_functions())
 
 
+def declared_param_kinds():
+    """name -> list of 'p' (pointer), 'i' (int / enum), 'f' (float), 'd' (double), 's' (size_t)
+    for every function the header declares."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"^[A-Za-z_][\w \t\*]*?\b([a-z_][a-z0-9_]*)\s*\(([^)]*)\)\s*;", text,
+                         flags=re.M):
+        params = [x.strip() for x in m.group(2).split(",") if x.strip() and x.strip() != "void"]
+        kinds = []
+        for prm in params:
+            if "*" in prm:
+                kinds.append("p")
+            elif prm.startswith("size_t"):
+                kinds.append("s")
+            elif prm.startswith("double"):
+                kinds.append("d")
+            elif prm.startswith("float"):
+                kinds.append("f")
+            else:
+                kinds.append("i")
+        out[m.group(1)] = kinds
+    return out
+
+
+def test_binding_signatures_match_the_header():
+    kinds = declared_param_kinds()
+    code = {ctypes.c_void_p: "p", ctypes.c_int: "i", ctypes.c_float: "f", ctypes.c_double: "d",
+            ctypes.c_size_t: "s"}
+    assert set(kinds) == set(binding.SIGNATURES)
+    for name, (_, args) in binding.SIGNATURES.items():
+        assert [code[a] for a in args] == kinds[name], name
+
+
 def _fwd(lib, q=P, k=P, v=P, ve=None, gate=None, o=P, lse=P, B=1, T=8, H=1, D=64, W=4, scale=0.125,
          dt=1, doc=None):
     return lib.swa_fwd(q, k, v, ve, gate, doc, o, lse, B, T, H, D, W, scale, dt, None)
