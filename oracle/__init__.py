@@ -13,14 +13,15 @@ Every function here is pinned by the ``-m "not gpu"`` tests in
 
 from .prologue import (rope_angles, rope, rope_transpose, rms_norm, rms_norm_bwd,
                        rope_qknorm, rope_qknorm_bwd, round_bf16)
-from .gate import ve_gate, ve_gate_bwd, apply_gate
+from .gate import ve_gate, ve_gate_bwd, apply_gate, ve_lookup, ve_table_grad
 from .attention import (window_mask, segment_ids, visible_mask, attention_fwd,
                         attention_fwd_online, attention_bwd, attention_probs, pair_count)
 from .layer import layer_fwd, layer_bwd
 
 __all__ = [
     "rope_angles", "rope", "rope_transpose", "rms_norm", "rms_norm_bwd", "rope_qknorm",
-    "rope_qknorm_bwd", "round_bf16", "ve_gate", "ve_gate_bwd", "apply_gate", "window_mask",
+    "rope_qknorm_bwd", "round_bf16", "ve_gate", "ve_gate_bwd", "apply_gate", "ve_lookup",
+    "ve_table_grad", "window_mask",
     "segment_ids", "visible_mask",
     "attention_fwd", "attention_fwd_online", "attention_bwd", "attention_probs", "pair_count",
     "layer_fwd", "layer_bwd",

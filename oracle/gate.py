@@ -50,3 +50,26 @@ def ve_gate_bwd(x32: np.ndarray, Wg: np.ndarray, g: np.ndarray, dv_eff: np.ndarr
     dWg = np.einsum("btc,bth->ch", x32, dz)
     dx32 = np.einsum("bth,ch->btc", dz, Wg)
     return dv, dve, dg, dWg, dx32
+
+
+def ve_lookup(table: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    """ve[b, t] = table[ids[b, t]]: the value-embedding row of each token (B, T, H*D).
+
+    The write-up's ``value_embeds[layer_idx](token_ids)`` is an embedding lookup; reading:
+    ids outside [0, rows) contribute a zero row (they never occur for valid tokens).
+    """
+    ids = np.asarray(ids)
+    ok = (ids >= 0) & (ids < table.shape[0])
+    out = table[np.where(ok, ids, 0)]
+    return np.where(ok[..., None], out, 0.0)
+
+
+def ve_table_grad(dve: np.ndarray, ids: np.ndarray, rows: int) -> np.ndarray:
+    """Gradient of the table from the per-token gradients: dtable[v] = sum of dve[b, t] over the
+    tokens with ids[b, t] == v (invalid ids contribute nothing)."""
+    ids = np.asarray(ids).reshape(-1)
+    flat = dve.reshape(ids.shape[0], -1)
+    out = np.zeros((rows, flat.shape[1]))
+    ok = (ids >= 0) & (ids < rows)
+    np.add.at(out, ids[ok], flat[ok])
+    return out
