@@ -46,9 +46,10 @@ def layer_list(name: str):
                          "(18 x 1024, 6 x 2048), B=16, T=2048, H=12, D=128")
     wl = WORKLOADS[name]
     return dict(B=wl.B, T=wl.T, H=wl.H, D=wl.D, gate=wl.gate, windows=[wl.window],
-                doc_mean=wl.doc_mean, seed=wl.seed,
+                doc_mean=wl.doc_mean, seed=wl.seed, ve_table=wl.ve_table,
                 desc=f"{name}: B={wl.B}, T={wl.T}, H={wl.H}, D={wl.D}, window {wl.window}"
                      + (", value-embedding gate" if wl.gate else "")
+                     + (" reading the (50304, H*D) table by token id" if wl.ve_table else "")
                      + (f", packed rows of documents averaging {wl.doc_mean} tokens"
                         if wl.doc_mean else ""))
 
@@ -96,7 +97,10 @@ def make_layers(cfg, torch, seed0=1000):
             t["Wg"] = torch.randn((32, H), generator=g, device="cuda") * 0.02
             table = torch.randn((50304, H * D), generator=g, device="cuda").to(torch.bfloat16)
             ids = torch.randint(0, 50304, (B, T), generator=g, device="cuda")
-            t["ve"] = table[ids].contiguous()
+            if cfg.get("ve_table"):
+                t["ve"], t["ids"] = table, ids.to(torch.int32)
+            else:
+                t["ve"] = table[ids].contiguous()
             del table
             t["gate"] = torch.empty((B, T, H), dtype=torch.float32, device="cuda")
         t["W"] = W
@@ -123,7 +127,12 @@ def run_bench(args):
     # gradient buffers shared by all layers
     g = {n: torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
          for n in ("dqn", "dkn", "dv", "dq", "dk")}
-    if cfg["gate"]:
+    if cfg.get("ve_table"):
+        # the table gradient is accumulated into (zeroed once; steps keep adding to it)
+        g["dve"] = torch.zeros((50304, H * D), dtype=torch.float32, device="cuda")
+        g["dgate"] = torch.empty((B, T, H), dtype=torch.float32, device="cuda")
+        g["dWg"] = torch.empty((32, H), dtype=torch.float32, device="cuda")
+    elif cfg["gate"]:
         g["dve"] = torch.empty((B, T, H * D), dtype=torch.bfloat16, device="cuda")
         g["dgate"] = torch.empty((B, T, H), dtype=torch.float32, device="cuda")
         g["dWg"] = torch.empty((32, H), dtype=torch.float32, device="cuda")
@@ -143,7 +152,8 @@ def run_bench(args):
     def step(rec):
         # forward, layers in order
         for li, t in enumerate(layers):
-            bounds = t.get("bounds")
+            bounds, ids = t.get("bounds"), t.get("ids")
+            rows = 0 if ids is None else t["ve"].shape[0]
             call("rope_qknorm_fwd", P(t["q"]), P(t["k"]), P(cs), P(t["qn"]), P(t["kn"]), B, T, H, D,
                  1e-6, sw.SWA_BF16, stream)
             ve = gate = None
@@ -152,14 +162,15 @@ def run_bench(args):
                      H, D, sw.SWA_BF16, stream)
                 ve, gate = t["ve"], t["gate"]
             if rec: rec["fwd"][li][0].record()
-            call("swa_fwd", P(t["qn"]), P(t["kn"]), P(t["v"]), P(ve), P(gate), P(bounds), P(t["o"]),
-                 P(t["lse"]),
+            call("swa_fwd", P(t["qn"]), P(t["kn"]), P(t["v"]), P(ve), P(gate), P(ids), rows,
+                 P(bounds), P(t["o"]), P(t["lse"]),
                  B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
             if rec: rec["fwd"][li][1].record()
         # backward, layers in reverse
         for li in reversed(range(len(layers))):
             t = layers[li]
-            bounds = t.get("bounds")
+            bounds, ids = t.get("bounds"), t.get("ids")
+            rows = 0 if ids is None else t["ve"].shape[0]
             ve = gate = dve = dgate = None
             if cfg["gate"]:
                 ve, gate, dve, dgate = t["ve"], t["gate"], g["dve"], g["dgate"]
@@ -167,13 +178,13 @@ def run_bench(args):
             call("swa_bwd_preprocess", P(t["o"]), P(t["dO"]), P(t["lse"]), P(ws), nws, B, T, H, D,
                  sw.SWA_BF16, stream)
             if rec: rec["bwd"][li][1].record()
-            call("swa_bwd_dkdv", P(t["qn"]), P(t["kn"]), P(t["v"]), P(ve), P(gate), P(bounds),
-                 P(t["lse"]),
+            call("swa_bwd_dkdv", P(t["qn"]), P(t["kn"]), P(t["v"]), P(ve), P(gate), P(ids), rows,
+                 P(bounds), P(t["lse"]),
                  P(t["dO"]), P(g["dkn"]), P(g["dv"]), P(dve), P(dgate), P(ws), nws,
                  B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
             if rec: rec["bwd"][li][2].record()
-            call("swa_bwd_dq", P(t["qn"]), P(t["kn"]), P(t["v"]), P(ve), P(gate), P(bounds),
-                 P(t["lse"]),
+            call("swa_bwd_dq", P(t["qn"]), P(t["kn"]), P(t["v"]), P(ve), P(gate), P(ids), rows,
+                 P(bounds), P(t["lse"]),
                  P(t["dO"]), P(g["dqn"]), P(ws), nws, B, T, H, D, t["W"], scale, sw.SWA_BF16,
                  stream)
             if rec: rec["bwd"][li][3].record()
@@ -462,7 +473,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="sssl24",
                     choices=["sssl24", "d24_short", "d24_full", "gpt2_124m", "d24_short_ve",
-                             "d24_short_doc", "d24_decode"])
+                             "d24_short_doc", "d24_short_vetable", "d24_decode"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",

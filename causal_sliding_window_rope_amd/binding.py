@@ -33,15 +33,15 @@ SIGNATURES = {
     "ve_gate_v": (_I, [_P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "ve_gate_v_bwd": (_I, [_P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "swa_doc_bounds": (_I, [_P, _P, _I, _I, _P]),
-    "swa_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "swa_fwd": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "swa_bwd_workspace_size": (_S, [_I, _I, _I, _I, _I]),
-    "swa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
+    "swa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
                      _I, _I, _I, _I, _I, _F, _I, _P]),
     "swa_bwd_preprocess": (_I, [_P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _P]),
-    "swa_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
+    "swa_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _S,
                           _I, _I, _I, _I, _I, _F, _I, _P]),
-    "swa_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _F, _I,
-                        _P]),
+    "swa_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I,
+                        _F, _I, _P]),
     "swa_decode_prologue": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "swa_decode_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "swa_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _F, _I, _P]),
@@ -174,20 +174,35 @@ def swa_doc_bounds(doc_id, out=None):
     return bounds
 
 
+def _ve_table(ve, gate, ve_ids, B, T, H, D, dtype):
+    """Checks the value-embedding arguments; returns (ids pointer, table rows)."""
+    if ve is None:
+        if ve_ids is not None:
+            raise ValueError("ve_ids needs ve and gate")
+        return None, 0
+    _check(gate, "gate", (B, T, H), torch.float32)
+    if ve_ids is None:
+        _check(ve, "ve", (B, T, H * D), dtype)
+        return None, 0
+    _check(ve_ids, "ve_ids", (B, T), torch.int32)
+    _check(ve, "ve", (ve.shape[0], H * D), dtype)
+    return _ptr(ve_ids), ve.shape[0]
+
+
 def swa_fwd(q, k, v, window: int, scale: float | None = None, ve=None, gate=None, out=None,
-            lse=None, doc_bounds=None):
+            lse=None, doc_bounds=None, ve_ids=None):
+    """ve_ids (B, T) int32 selects the table mode: ve is then a (rows, H*D) table."""
     B, T, H, D = q.shape
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _check(t, n, (B, T, H, D), q.dtype)
-    if ve is not None:
-        _check(ve, "ve", (B, T, H * D), q.dtype)
-        _check(gate, "gate", (B, T, H), torch.float32)
+    ids, rows = _ve_table(ve, gate, ve_ids, B, T, H, D, q.dtype)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if lse is None else lse
     if doc_bounds is not None:
         _check(doc_bounds, "doc_bounds", (B, T, 2), torch.int32)
-    _call("swa_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), _ptr(doc_bounds), _ptr(o),
+    _call("swa_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), ids, rows, _ptr(doc_bounds),
+          _ptr(o),
           _ptr(lse), B, T, H, D, int(window), float(scale), _dt(q), _stream())
     return o, lse
 
@@ -196,26 +211,36 @@ def swa_bwd_workspace_size(B: int, T: int, H: int, D: int, dtype: torch.dtype) -
     return load().swa_bwd_workspace_size(B, T, H, D, SWA_BF16 if dtype == torch.bfloat16 else SWA_F32)
 
 
+def _grads(q, ve, ve_ids, B, T, H):
+    """Fresh gradient buffers; in the table mode dve is a zeroed float table gradient."""
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    if ve is None:
+        return dq, dk, dv, None, None
+    if ve_ids is None:
+        dve = torch.empty_like(ve)
+    else:
+        dve = torch.zeros(ve.shape, dtype=torch.float32, device=q.device)
+    return dq, dk, dv, dve, torch.empty((B, T, H), dtype=torch.float32, device=q.device)
+
+
 def swa_bwd(q, k, v, o, lse, dO, window: int, scale: float | None = None, ve=None, gate=None,
-            workspace=None, grads=None, doc_bounds=None):
-    """Returns (dq, dk, dv) or, with the gate, (dq, dk, dv, dve, dgate)."""
+            workspace=None, grads=None, doc_bounds=None, ve_ids=None):
+    """Returns (dq, dk, dv) or, with the gate, (dq, dk, dv, dve, dgate). With ve_ids, dve is the
+    (rows, H*D) float table gradient, accumulated into (a given one is not zeroed)."""
     B, T, H, D = q.shape
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dO, "dO")):
         _check(t, n, (B, T, H, D), q.dtype)
     _check(lse, "lse", (B, H, T), torch.float32)
+    ids, rows = _ve_table(ve, gate, ve_ids, B, T, H, D, q.dtype)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     ws_bytes = swa_bwd_workspace_size(B, T, H, D, q.dtype)
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    if grads is None:
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        dve = torch.empty_like(ve) if ve is not None else None
-        dgate = torch.empty((B, T, H), dtype=torch.float32, device=q.device) if ve is not None else None
-    else:
-        dq, dk, dv, dve, dgate = grads
+    dq, dk, dv, dve, dgate = _grads(q, ve, ve_ids, B, T, H) if grads is None else grads
     if doc_bounds is not None:
         _check(doc_bounds, "doc_bounds", (B, T, 2), torch.int32)
-    _call("swa_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), _ptr(doc_bounds), _ptr(o),
+    _call("swa_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), ids, rows,
+          _ptr(doc_bounds), _ptr(o),
           _ptr(lse), _ptr(dO),
           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dve), _ptr(dgate), _ptr(workspace),
           workspace.numel() * workspace.element_size(), B, T, H, D, int(window), float(scale),
@@ -226,29 +251,27 @@ def swa_bwd(q, k, v, o, lse, dO, window: int, scale: float | None = None, ve=Non
 
 
 def swa_bwd_stages(q, k, v, o, lse, dO, window: int, scale: float | None = None, ve=None,
-                   gate=None, workspace=None, grads=None, doc_bounds=None):
+                   gate=None, workspace=None, grads=None, doc_bounds=None, ve_ids=None):
     """swa_bwd as its three C-ABI stages: preprocess, dK/dV, dQ."""
     B, T, H, D = q.shape
+    ids, rows = _ve_table(ve, gate, ve_ids, B, T, H, D, q.dtype)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     ws_bytes = swa_bwd_workspace_size(B, T, H, D, q.dtype)
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     nbytes = workspace.numel() * workspace.element_size()
-    if grads is None:
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        dve = torch.empty_like(ve) if ve is not None else None
-        dgate = torch.empty((B, T, H), dtype=torch.float32, device=q.device) if ve is not None else None
-    else:
-        dq, dk, dv, dve, dgate = grads
+    dq, dk, dv, dve, dgate = _grads(q, ve, ve_ids, B, T, H) if grads is None else grads
     st = _stream()
     dt = _dt(q)
     _call("swa_bwd_preprocess", _ptr(o), _ptr(dO), _ptr(lse), _ptr(workspace), nbytes, B, T, H, D, dt,
           st)
-    _call("swa_bwd_dkdv", _ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), _ptr(doc_bounds),
+    _call("swa_bwd_dkdv", _ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), ids, rows,
+          _ptr(doc_bounds),
           _ptr(lse), _ptr(dO),
           _ptr(dk), _ptr(dv), _ptr(dve), _ptr(dgate), _ptr(workspace), nbytes, B, T, H, D,
           int(window), float(scale), dt, st)
-    _call("swa_bwd_dq", _ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), _ptr(doc_bounds),
+    _call("swa_bwd_dq", _ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), ids, rows,
+          _ptr(doc_bounds),
           _ptr(lse), _ptr(dO),
           _ptr(dq), _ptr(workspace), nbytes, B, T, H, D, int(window), float(scale), dt, st)
     if ve is not None:

@@ -171,9 +171,26 @@ int swa_doc_bounds(const int* doc_id, int* doc_bounds, int B, int T, void* strea
   return hip_status(swa::launch_doc_bounds(doc_id, doc_bounds, B, T, (hipStream_t)stream), fn);
 }
 
+// Value-embedding table mode: with ve_ids, ve is a (ve_rows, H*D) table indexed by the token
+// ids and the backward's dve is its float gradient; without, ve_rows must be 0.
+static int check_ve_table(const char* fn, const void* ve, const int* ve_ids, int ve_rows, int H,
+                          int D, swa::AttnShape* a) {
+  if (!ve_ids) {
+    if (ve_rows != 0) return fail(SWA_ERR_INVALID_ARG, "%s: ve_rows must be 0 without ve_ids", fn);
+    return ok();
+  }
+  if (!ve) return fail(SWA_ERR_INVALID_ARG, "%s: ve_ids needs ve and gate", fn);
+  if (ve_rows < 1) return fail(SWA_ERR_INVALID_ARG, "%s: ve_rows must be >= 1 with ve_ids", fn);
+  if ((long long)ve_rows * H * D >= (1LL << 40))
+    return fail(SWA_ERR_UNSUPPORTED, "%s: value-embedding table too large", fn);
+  a->ve_ids = ve_ids;
+  a->ve_rows = ve_rows;
+  return ok();
+}
+
 int swa_fwd(const void* q, const void* k, const void* v, const void* ve, const float* gate,
-            const int* doc_bounds, void* o, float* lse, int B, int T, int H, int D, int window,
-            float scale, swa_dtype dtype, void* stream) {
+            const int* ve_ids, int ve_rows, const int* doc_bounds, void* o, float* lse, int B,
+            int T, int H, int D, int window, float scale, swa_dtype dtype, void* stream) {
   const char* fn = "swa_fwd";
   SWA_TRY(check_shape(fn, B, T, H, D, dtype));
   SWA_TRY(need(fn, "q", q)); SWA_TRY(need(fn, "k", k)); SWA_TRY(need(fn, "v", v));
@@ -183,6 +200,7 @@ int swa_fwd(const void* q, const void* k, const void* v, const void* ve, const f
   SWA_TRY(opt(fn, "ve", ve)); SWA_TRY(opt(fn, "doc_bounds", doc_bounds));
   swa::AttnShape a{B, T, H, D, 0, scale};
   a.bounds = doc_bounds;
+  SWA_TRY(check_ve_table(fn, ve, ve_ids, ve_rows, H, D, &a));
   SWA_TRY(check_window_scale(fn, window, scale, T, &a.window));
   return hip_status(swa::launch_fwd(a, q, k, v, ve, gate, o, lse, dtype == SWA_BF16,
                                     (hipStream_t)stream), fn);
@@ -194,8 +212,8 @@ size_t swa_bwd_workspace_size(int B, int T, int H, int D, swa_dtype dtype) {
 }
 
 static int check_bwd(const char* fn, const void* q, const void* k, const void* v, const void* ve,
-                     const float* gate, const int* doc_bounds, const void* o, const float* lse,
-                     const void* dO,
+                     const float* gate, const int* ve_ids, int ve_rows, const int* doc_bounds,
+                     const void* o, const float* lse, const void* dO,
                      const void* dq, const void* dk, const void* dv, const void* dve,
                      const float* dgate, const void* workspace, size_t ws_bytes, int B, int T,
                      int H, int D, int window, float scale, swa_dtype dtype, swa::AttnShape* a) {
@@ -213,19 +231,21 @@ static int check_bwd(const char* fn, const void* q, const void* k, const void* v
   SWA_TRY(opt(fn, "doc_bounds", doc_bounds));
   *a = swa::AttnShape{B, T, H, D, 0, scale};
   a->bounds = doc_bounds;
+  SWA_TRY(check_ve_table(fn, ve, ve_ids, ve_rows, H, D, a));
   SWA_TRY(check_window_scale(fn, window, scale, T, &a->window));
   return check_ws(fn, workspace, ws_bytes, B, T, H, D, dtype);
 }
 
 int swa_bwd(const void* q, const void* k, const void* v, const void* ve, const float* gate,
-            const int* doc_bounds, const void* o, const float* lse, const void* dO, void* dq,
-            void* dk, void* dv, void* dve, float* dgate, void* workspace, size_t ws_bytes, int B,
-            int T, int H, int D, int window, float scale, swa_dtype dtype, void* stream) {
+            const int* ve_ids, int ve_rows, const int* doc_bounds, const void* o, const float* lse,
+            const void* dO, void* dq, void* dk, void* dv, void* dve, float* dgate, void* workspace,
+            size_t ws_bytes, int B, int T, int H, int D, int window, float scale, swa_dtype dtype,
+            void* stream) {
   const char* fn = "swa_bwd";
   swa::AttnShape a;
   SWA_TRY(need(fn, "o", o));
-  SWA_TRY(check_bwd(fn, q, k, v, ve, gate, doc_bounds, o, lse, dO, dq, dk, dv, dve, dgate, workspace,
-                    ws_bytes, B, T, H, D, window, scale, dtype, &a));
+  SWA_TRY(check_bwd(fn, q, k, v, ve, gate, ve_ids, ve_rows, doc_bounds, o, lse, dO, dq, dk, dv, dve,
+                    dgate, workspace, ws_bytes, B, T, H, D, window, scale, dtype, &a));
   const bool bf = dtype == SWA_BF16;
   const hipStream_t s = (hipStream_t)stream;
   hipError_t e = swa::launch_bwd_pre(a, o, dO, lse, workspace, bf, s);
@@ -246,22 +266,23 @@ int swa_bwd_preprocess(const void* o, const void* dO, const float* lse, void* wo
 }
 
 int swa_bwd_dkdv(const void* q, const void* k, const void* v, const void* ve, const float* gate,
-                 const int* doc_bounds, const float* lse, const void* dO, void* dk, void* dv,
-                 void* dve, float* dgate, void* workspace, size_t ws_bytes, int B, int T, int H,
-                 int D, int window, float scale, swa_dtype dtype, void* stream) {
+                 const int* ve_ids, int ve_rows, const int* doc_bounds, const float* lse,
+                 const void* dO, void* dk, void* dv, void* dve, float* dgate, void* workspace,
+                 size_t ws_bytes, int B, int T, int H, int D, int window, float scale,
+                 swa_dtype dtype, void* stream) {
   const char* fn = "swa_bwd_dkdv";
   swa::AttnShape a;
   // dq is not used by this stage; dk stands in for it in the shared checks
-  SWA_TRY(check_bwd(fn, q, k, v, ve, gate, doc_bounds, nullptr, lse, dO, dk, dk, dv, dve, dgate, workspace,
-                    ws_bytes, B, T, H, D, window, scale, dtype, &a));
+  SWA_TRY(check_bwd(fn, q, k, v, ve, gate, ve_ids, ve_rows, doc_bounds, nullptr, lse, dO, dk, dk, dv,
+                    dve, dgate, workspace, ws_bytes, B, T, H, D, window, scale, dtype, &a));
   return hip_status(swa::launch_bwd_dkdv(a, q, k, v, ve, gate, lse, dO, dk, dv, dve, dgate,
                                          workspace, dtype == SWA_BF16, (hipStream_t)stream), fn);
 }
 
 int swa_bwd_dq(const void* q, const void* k, const void* v, const void* ve, const float* gate,
-               const int* doc_bounds, const float* lse, const void* dO, void* dq, void* workspace,
-               size_t ws_bytes, int B, int T, int H, int D, int window, float scale,
-               swa_dtype dtype, void* stream) {
+               const int* ve_ids, int ve_rows, const int* doc_bounds, const float* lse,
+               const void* dO, void* dq, void* workspace, size_t ws_bytes, int B, int T, int H,
+               int D, int window, float scale, swa_dtype dtype, void* stream) {
   const char* fn = "swa_bwd_dq";
   SWA_TRY(check_shape(fn, B, T, H, D, dtype));
   SWA_TRY(need(fn, "q", q)); SWA_TRY(need(fn, "k", k)); SWA_TRY(need(fn, "v", v));
@@ -271,6 +292,7 @@ int swa_bwd_dq(const void* q, const void* k, const void* v, const void* ve, cons
   SWA_TRY(opt(fn, "ve", ve)); SWA_TRY(opt(fn, "doc_bounds", doc_bounds));
   swa::AttnShape a{B, T, H, D, 0, scale};
   a.bounds = doc_bounds;
+  SWA_TRY(check_ve_table(fn, ve, ve_ids, ve_rows, H, D, &a));
   SWA_TRY(check_window_scale(fn, window, scale, T, &a.window));
   SWA_TRY(check_ws(fn, workspace, ws_bytes, B, T, H, D, dtype));
   return hip_status(swa::launch_bwd_dq(a, q, k, v, ve, gate, lse, dO, dq, workspace,

@@ -87,6 +87,9 @@ struct Params {
   const float* nlse2; const float* ndelta; const bf16* dO;   // row terms, negated
   const int* bounds;   // per-token document [start, end) (document masking only)
   bf16* dk; bf16* dv; bf16* dve; float* dgate;
+  const int* ve_ids;   // table mode: ve is (ve_rows, H*D), dve_tab the float table gradient
+  int ve_rows;
+  float* dve_tab;
   int B, T, H, window, nkb;
   float c;       // scale * log2(e)
   float scale;
@@ -167,7 +170,9 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dkdv_bf16_kernel(Params 
       uint4 kk = *reinterpret_cast<const uint4*>(p.k + off);
       uint4 vv = *reinterpret_cast<const uint4*>(p.v + off);
       if constexpr (GATE) {
-        const uint4 ee = *reinterpret_cast<const uint4*>(p.ve + off);
+        const bf16* er = ve_row<D>(p.ve, p.ve_ids, p.ve_rows, b, T, H, h, min(mykey, T - 1));
+        const uint4 ee = er ? *reinterpret_cast<const uint4*>(er + 16 * ks + 8 * hi)
+                            : make_uint4(0, 0, 0, 0);
         vv.x = pack_bf2(fmaf(gk, bf_lo(ee.x), bf_lo(vv.x)), fmaf(gk, bf_hi(ee.x), bf_hi(vv.x)));
         vv.y = pack_bf2(fmaf(gk, bf_lo(ee.y), bf_lo(vv.y)), fmaf(gk, bf_hi(ee.y), bf_hi(vv.y)));
         vv.z = pack_bf2(fmaf(gk, bf_lo(ee.z), bf_lo(vv.z)), fmaf(gk, bf_hi(ee.z), bf_hi(vv.z)));
@@ -361,15 +366,24 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dkdv_bf16_kernel(Params 
     if (key >= T) continue;
     const size_t row = head0 + (size_t)key * rs;
     float gsum = 0.f, gkey = 0.f;
-    if constexpr (GATE) gkey = p.gate[(size_t)(b * T + key) * H + h];
+    const bf16* er = nullptr;
+    if constexpr (GATE) {
+      gkey = p.gate[(size_t)(b * T + key) * H + h];
+      er = ve_row<D>(p.ve, p.ve_ids, p.ve_rows, b, T, H, h, key);
+    }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const size_t off = row + db * 32 + l32;
       p.dk[off] = (bf16)(dk[db][i] * p.scale);
       p.dv[off] = (bf16)dv[db][i];
       if constexpr (GATE) {
-        p.dve[off] = (bf16)(gkey * dv[db][i]);
-        gsum = fmaf(dv[db][i], (float)p.ve[off], gsum);
+        if (p.ve_ids) {
+          // table mode: tokens sharing an id add into one row (float atomics)
+          if (er) atomicAdd(p.dve_tab + (er - p.ve) + db * 32 + l32, gkey * dv[db][i]);
+        } else {
+          p.dve[off] = (bf16)(gkey * dv[db][i]);
+        }
+        if (er) gsum = fmaf(dv[db][i], (float)er[db * 32 + l32], gsum);
       }
     }
     if constexpr (GATE) {
@@ -401,18 +415,20 @@ __global__ void __launch_bounds__(64) bwd_dkdv_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ ve, const float* __restrict__ gate, const float* __restrict__ lse,
     const float* __restrict__ ndelta, const float* __restrict__ dO, const int* __restrict__ bounds,
+    const int* __restrict__ ve_ids, int ve_rows,
     float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dve,
     float* __restrict__ dgate, int T, int H, int W, float scale) {
   constexpr int PER = D / 64;
   const int j = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, lane = threadIdx.x;
   const size_t krow = ((size_t)b * T + j) * H + h;
   const float g = gate ? gate[krow] : 0.f;
+  const float* er = gate ? ve_row<D>(ve, ve_ids, ve_rows, b, T, H, h, j) : nullptr;
   float kv[PER], vv[PER], ak[PER], av[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     kv[e] = k[krow * D + lane + 64 * e];
     vv[e] = v[krow * D + lane + 64 * e];
-    if (gate) vv[e] = fmaf(g, ve[krow * D + lane + 64 * e], vv[e]);
+    if (er) vv[e] = fmaf(g, er[lane + 64 * e], vv[e]);
     ak[e] = 0.f; av[e] = 0.f;
   }
   const int i1 = min(min(T - 1, j + W - 1), bounds ? bounds[2 * ((size_t)b * T + j) + 1] - 1 : T - 1);
@@ -434,8 +450,9 @@ __global__ void __launch_bounds__(64) bwd_dkdv_f32_kernel(
     dk[krow * D + lane + 64 * e] = ak[e] * scale;
     dv[krow * D + lane + 64 * e] = av[e];
     if (gate) {
-      dve[krow * D + lane + 64 * e] = g * av[e];
-      gs = fmaf(av[e], ve[krow * D + lane + 64 * e], gs);
+      if (!ve_ids) dve[krow * D + lane + 64 * e] = g * av[e];
+      else if (er) atomicAdd(dve + (er - ve) + lane + 64 * e, g * av[e]);
+      if (er) gs = fmaf(av[e], er[lane + 64 * e], gs);
     }
   }
   if (gate) {
@@ -450,7 +467,8 @@ __global__ void __launch_bounds__(64) bwd_dq_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ ve, const float* __restrict__ gate, const float* __restrict__ lse,
     const float* __restrict__ ndelta, const float* __restrict__ dO, const int* __restrict__ bounds,
-    float* __restrict__ dq, int T, int H, int W, float scale) {
+    const int* __restrict__ ve_ids, int ve_rows, float* __restrict__ dq, int T, int H, int W,
+    float scale) {
   constexpr int PER = D / 64;
   const int i = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, lane = threadIdx.x;
   const size_t qrow = ((size_t)b * T + i) * H + h;
@@ -469,10 +487,11 @@ __global__ void __launch_bounds__(64) bwd_dq_f32_kernel(
     const float pij = expf(s - L);
     float dp = 0.f;
     const float g = gate ? gate[krow] : 0.f;
+    const float* er = gate ? ve_row<D>(ve, ve_ids, ve_rows, b, T, H, h, j) : nullptr;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
       float vv = v[krow * D + lane + 64 * e];
-      if (gate) vv = fmaf(g, ve[krow * D + lane + 64 * e], vv);
+      if (er) vv = fmaf(g, er[lane + 64 * e], vv);
       dp = fmaf(ov[e], vv, dp);
     }
 #pragma unroll
@@ -559,6 +578,7 @@ hipError_t launch_bwd_dkdv(const AttnShape& a, const void* q, const void* k, con
     p.gate = gate; p.nlse2 = w.nlse2; p.ndelta = w.ndelta; p.dO = (const bf16*)dO;
     p.bounds = a.bounds;
     p.dk = (bf16*)dk; p.dv = (bf16*)dv; p.dve = (bf16*)dve; p.dgate = dgate;
+    p.ve_ids = a.ve_ids; p.ve_rows = a.ve_rows; p.dve_tab = (float*)dve;
     p.B = B; p.T = T; p.H = H; p.window = a.window;
     p.nkb = (T + bwdk::BNK - 1) / bwdk::BNK;
     p.c = a.scale * kLog2e;
@@ -571,11 +591,13 @@ hipError_t launch_bwd_dkdv(const AttnShape& a, const void* q, const void* k, con
   if (D == 64)
     hipLaunchKernelGGL(bwd_dkdv_f32_kernel<64>, grid, dim3(64), 0, s, (const float*)q, (const float*)k,
                        (const float*)v, (const float*)ve, gate, lse, w.ndelta, (const float*)dO,
-                       a.bounds, (float*)dk, (float*)dv, (float*)dve, dgate, T, H, a.window, a.scale);
+                       a.bounds, a.ve_ids, a.ve_rows, (float*)dk, (float*)dv, (float*)dve, dgate, T, H,
+                       a.window, a.scale);
   else
     hipLaunchKernelGGL(bwd_dkdv_f32_kernel<128>, grid, dim3(64), 0, s, (const float*)q, (const float*)k,
                        (const float*)v, (const float*)ve, gate, lse, w.ndelta, (const float*)dO,
-                       a.bounds, (float*)dk, (float*)dv, (float*)dve, dgate, T, H, a.window, a.scale);
+                       a.bounds, a.ve_ids, a.ve_rows, (float*)dk, (float*)dv, (float*)dve, dgate, T, H,
+                       a.window, a.scale);
   return hipGetLastError();
 }
 
@@ -589,11 +611,11 @@ hipError_t launch_bwd_dq(const AttnShape& a, const void* q, const void* k, const
   if (D == 64)
     hipLaunchKernelGGL(bwd_dq_f32_kernel<64>, grid, dim3(64), 0, s, (const float*)q, (const float*)k,
                        (const float*)v, (const float*)ve, gate, lse, w.ndelta, (const float*)dO,
-                       a.bounds, (float*)dq, T, H, a.window, a.scale);
+                       a.bounds, a.ve_ids, a.ve_rows, (float*)dq, T, H, a.window, a.scale);
   else
     hipLaunchKernelGGL(bwd_dq_f32_kernel<128>, grid, dim3(64), 0, s, (const float*)q, (const float*)k,
                        (const float*)v, (const float*)ve, gate, lse, w.ndelta, (const float*)dO,
-                       a.bounds, (float*)dq, T, H, a.window, a.scale);
+                       a.bounds, a.ve_ids, a.ve_rows, (float*)dq, T, H, a.window, a.scale);
   return hipGetLastError();
 }
 

@@ -113,6 +113,19 @@ __device__ __forceinline__ void ds_store_b64(lds_t<bf16>* p, unsigned long long 
   asm volatile("ds_write_b64 %0, %1" : : "v"((unsigned)(size_t)p), "v"(v) : "memory");
 }
 
+// Value-embedding row (D bf16 of head h) of token t of sequence b: either in the (B, T, H*D)
+// tensor, or, with token ids, row ids[b*T + t] of a (rows, H*D) table; nullptr for an id outside
+// the table (such a token gets a zero value embedding and no table gradient).
+template <int D, typename E>
+__device__ __forceinline__ const E* ve_row(const E* ve, const int* ids, int rows, int b, int T,
+                                           int H, int h, int t) {
+  if (ids) {
+    const int id = ids[(size_t)b * T + t];
+    return (unsigned)id < (unsigned)rows ? ve + ((size_t)id * H + h) * D : nullptr;
+  }
+  return ve + (((size_t)b * T + t) * H + h) * D;
+}
+
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

@@ -32,6 +32,8 @@ template <int D> struct Cfg {
 struct Params {
   const bf16* q; const bf16* k; const bf16* v; const bf16* ve; const float* gate;
   const int* bounds;   // per-token document [start, end) (document masking only)
+  const int* ve_ids;   // value-embedding table rows per token (table mode only)
+  int ve_rows;
   const bf16* dO; const float* nlse2; const float* ndelta;   // row terms, negated
   bf16* dq;
   int B, T, H, window, nqb;
@@ -83,8 +85,11 @@ struct Tiles {
         const int grow = min(kt * BN + r, p.T - 1);
         const size_t goff = (size_t)grow * rs + 8 * c;
         const uint4 a = *reinterpret_cast<const uint4*>(vbase + goff);
-        const uint4 e = *reinterpret_cast<const uint4*>(p.ve + (vbase - p.v) + goff);
-        const float g = p.gate[(vbase - p.v) / D + (size_t)grow * p.H];
+        const size_t hb = (size_t)(vbase - p.v) / D;   // b * T * H + h
+        const int bb = (int)(hb / ((size_t)p.T * p.H)), hh = (int)(hb - (size_t)bb * p.T * p.H);
+        const bf16* er = ve_row<D>(p.ve, p.ve_ids, p.ve_rows, bb, p.T, p.H, hh, grow);
+        const uint4 e = er ? *reinterpret_cast<const uint4*>(er + 8 * c) : make_uint4(0, 0, 0, 0);
+        const float g = p.gate[hb + (size_t)grow * p.H];
         u32x4 o;
         o.x = pack_bf2(fmaf(g, bf_lo(e.x), bf_lo(a.x)), fmaf(g, bf_hi(e.x), bf_hi(a.x)));
         o.y = pack_bf2(fmaf(g, bf_lo(e.y), bf_lo(a.y)), fmaf(g, bf_hi(e.y), bf_hi(a.y)));
@@ -285,6 +290,7 @@ hipError_t launch_dq_bf16(const AttnShape& a, const void* q, const void* k, cons
                           const float* ndelta, void* dq, hipStream_t s) {
   dqk::Params p;
   p.q = (const bf16*)q; p.k = (const bf16*)k; p.v = (const bf16*)v; p.ve = (const bf16*)ve;
+  p.ve_ids = a.ve_ids; p.ve_rows = a.ve_rows;
   p.gate = gate; p.bounds = a.bounds; p.dO = (const bf16*)dO; p.nlse2 = nlse2; p.ndelta = ndelta; p.dq = (bf16*)dq;
   p.B = a.B; p.T = a.T; p.H = a.H; p.window = a.window;
   p.nqb = (a.T + dqk::BM - 1) / dqk::BM;

@@ -44,6 +44,8 @@ template <int D> struct Cfg {
 struct Params {
   const bf16* q; const bf16* k; const bf16* v; const bf16* ve; const float* gate;
   const int* bounds;   // per-token document [start, end) (document masking only)
+  const int* ve_ids;   // value-embedding table rows per token (table mode only)
+  int ve_rows;
   bf16* o; float* lse;
   int B, T, H, window, nqb;
   float c;      // scale * log2(e)
@@ -102,8 +104,11 @@ struct Tiles {
         const int grow = min(kt * BN + r, T - 1);
         const size_t goff = (size_t)grow * rs + 8 * c;
         const uint4 a = *reinterpret_cast<const uint4*>(vbase + goff);
-        const uint4 e = *reinterpret_cast<const uint4*>(p.ve + (vbase - p.v) + goff);
-        const float g = p.gate[(vbase - p.v) / D + (size_t)grow * p.H];
+        const size_t hb = (size_t)(vbase - p.v) / D;   // b * T * H + h
+        const int bb = (int)(hb / ((size_t)p.T * p.H)), hh = (int)(hb - (size_t)bb * p.T * p.H);
+        const bf16* er = ve_row<D>(p.ve, p.ve_ids, p.ve_rows, bb, p.T, p.H, hh, grow);
+        const uint4 e = er ? *reinterpret_cast<const uint4*>(er + 8 * c) : make_uint4(0, 0, 0, 0);
+        const float g = p.gate[hb + (size_t)grow * p.H];
         u32x4 o;
         o.x = pack_bf2(fmaf(g, bf_lo(e.x), bf_lo(a.x)), fmaf(g, bf_hi(e.x), bf_hi(a.x)));
         o.y = pack_bf2(fmaf(g, bf_lo(e.y), bf_lo(a.y)), fmaf(g, bf_hi(e.y), bf_hi(a.y)));
@@ -375,6 +380,7 @@ __global__ void __launch_bounds__(64) fwd_f32_kernel(const float* __restrict__ q
                                                      const float* __restrict__ ve,
                                                      const float* __restrict__ gate,
                                                      const int* __restrict__ bounds,
+                                                     const int* __restrict__ ve_ids, int ve_rows,
                                                      float* __restrict__ o, float* __restrict__ lse,
                                                      int T, int H, int W, float scale) {
   constexpr int PER = D / 64;
@@ -398,10 +404,11 @@ __global__ void __launch_bounds__(64) fwd_f32_kernel(const float* __restrict__ q
     const float pj = expf(s - m_new);
     l = l * alpha + pj;
     const float g = gate ? gate[krow] : 0.f;
+    const float* er = gate ? ve_row<D>(ve, ve_ids, ve_rows, b, T, H, h, j) : nullptr;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
       float vv = v[krow * D + lane + 64 * e];
-      if (gate) vv = fmaf(g, ve[krow * D + lane + 64 * e], vv);
+      if (er) vv = fmaf(g, er[lane + 64 * e], vv);
       acc[e] = fmaf(acc[e], alpha, pj * vv);
     }
     m = m_new;
@@ -417,6 +424,7 @@ static hipError_t launch_fwd_bf16_t(const AttnShape& a, const void* q, const voi
                                     hipStream_t s) {
   fwdk::Params p;
   p.q = (const bf16*)q; p.k = (const bf16*)k; p.v = (const bf16*)v; p.ve = (const bf16*)ve;
+  p.ve_ids = a.ve_ids; p.ve_rows = a.ve_rows;
   p.gate = gate; p.bounds = a.bounds; p.o = (bf16*)o; p.lse = lse;
   p.B = a.B; p.T = a.T; p.H = a.H; p.window = a.window;
   p.nqb = (a.T + fwdk::BM - 1) / fwdk::BM;
@@ -445,11 +453,11 @@ hipError_t launch_fwd(const AttnShape& a, const void* q, const void* k, const vo
   dim3 grid(a.T, a.B * a.H);
   if (a.D == 64)
     hipLaunchKernelGGL(fwd_f32_kernel<64>, grid, dim3(64), 0, s, (const float*)q, (const float*)k,
-                       (const float*)v, (const float*)ve, gate, a.bounds, (float*)o, lse, a.T, a.H, a.window,
+                       (const float*)v, (const float*)ve, gate, a.bounds, a.ve_ids, a.ve_rows, (float*)o, lse, a.T, a.H, a.window,
                        a.scale);
   else
     hipLaunchKernelGGL(fwd_f32_kernel<128>, grid, dim3(64), 0, s, (const float*)q, (const float*)k,
-                       (const float*)v, (const float*)ve, gate, a.bounds, (float*)o, lse, a.T, a.H, a.window,
+                       (const float*)v, (const float*)ve, gate, a.bounds, a.ve_ids, a.ve_rows, (float*)o, lse, a.T, a.H, a.window,
                        a.scale);
   return hipGetLastError();
 }

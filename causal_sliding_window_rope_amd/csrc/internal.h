@@ -11,6 +11,10 @@ struct AttnShape {
   int window;   // already clamped: 1 <= window <= T
   float scale;
   const int* bounds = nullptr;   // optional per-token document [start, end), (B, T, 2) int32
+  // optional value-embedding table: ve is then (ve_rows, H*D) and token (b, t) uses row
+  // ve_ids[b*T + t]; the backward then adds gate * dv into a float (ve_rows, H*D) gradient
+  const int* ve_ids = nullptr;
+  int ve_rows = 0;
 };
 
 hipError_t launch_doc_bounds(const int* doc_id, int* bounds, int B, int T, hipStream_t s);

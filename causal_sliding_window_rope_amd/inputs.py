@@ -11,7 +11,8 @@ Recipe (the same on every machine):
 * draw order: q, k, v, dO (each (B, T, H, D)); for gated-value-embedding
   workloads the stream continues with x (B, T, C), Wg (32, H) scaled by 0.02
   (standard deviation 0.02), the embedding table (vocab, H*D), then token ids
-  ``integers(0, vocab, (B, T))``; ve = table[ids];
+  ``integers(0, vocab, (B, T))``; ve = table[ids]; table-mode workloads keep the
+  table and the ids (int32) instead of handing over the gathered rows;
 * document-masked workloads continue with the document layout: per row,
   documents of length max(1, round(lognormal(log(mean) - 1/2, 1))) tokens
   back to back, the last one cut at the row end (a BOS-aligned packed row);
@@ -57,6 +58,7 @@ class Workload:
     C: int = 0           # width of the block input x (gate workloads only)
     vocab: int = VOCAB
     doc_mean: int = 0    # mean document length of a packed row (0: one document per row)
+    ve_table: bool = False   # hand the value-embedding table and token ids to the kernels
 
     @property
     def scale(self) -> float:
@@ -76,6 +78,9 @@ WORKLOADS = {
     # the d24 short layer on BOS-aligned rows packing documents of ~512 tokens on average
     "d24_short_doc": Workload("d24_short_doc", B=16, T=2048, H=12, D=128, window=1024,
                               dtype="bf16", seed=7, doc_mean=512),
+    # the gated layer reading its value embedding from the (vocab, H*D) table by token id
+    "d24_short_vetable": Workload("d24_short_vetable", B=16, T=2048, H=12, D=128, window=1024,
+                                  dtype="bf16", seed=5, gate=True, C=1536, ve_table=True),
 }
 
 
@@ -112,6 +117,9 @@ def make_inputs(wl: Workload, heads: tuple[int, int] | None = None) -> dict[str,
             table = round_to_bf16(table)
         out["ve"] = table[ids]
         out["ids"] = ids
+        if wl.ve_table:
+            out["table"] = table
+            out["ids"] = ids.astype(np.int32)
         del table
     if wl.doc_mean > 0:
         out["doc_id"] = doc_layout(rng, wl.B, wl.T, wl.doc_mean)
@@ -148,8 +156,9 @@ def doc_layout(rng, B: int, T: int, mean_len: float) -> np.ndarray:
 
 
 def small_workload(B: int, T: int, H: int, D: int, window: int, dtype: str, seed: int,
-                   gate: bool = False, C: int = 64, doc_mean: int = 0) -> Workload:
+                   gate: bool = False, C: int = 64, doc_mean: int = 0, ve_table: bool = False,
+                   vocab: int = VOCAB) -> Workload:
     """A parity-test case with arbitrary (small) sizes and the same recipe."""
     return Workload(f"case_B{B}_T{T}_H{H}_D{D}_W{window}_{dtype}", B=B, T=T, H=H, D=D,
                     window=window, dtype=dtype, seed=seed, gate=gate, C=C if gate else 0,
-                    doc_mean=doc_mean)
+                    doc_mean=doc_mean, ve_table=ve_table, vocab=vocab)

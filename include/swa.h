@@ -36,7 +36,8 @@
  *     a swa_status; on a non-zero status nothing was enqueued (except SWA_ERR_HIP, where a
  *     launch failed) and swa_last_error() describes the problem. No C++ exception crosses
  *     the ABI. Device pointers must be 16-byte aligned (128-bit vector access).
- *   - Gradients are overwritten, never accumulated into.
+ *   - Gradients are overwritten, never accumulated into (except the value-embedding table
+ *     gradient of swa_bwd / swa_bwd_dkdv in the table mode, see there).
  */
 #ifndef SWA_H_
 #define SWA_H_
@@ -142,14 +143,19 @@ int swa_doc_bounds(const int* doc_id, int* doc_bounds, int B, int T, void* strea
  *   O_i = sum_j exp(s_ij - lse_i) v_eff_j, v_eff = v (+ gate * ve when ve and gate are given).
  *   q, k, v: device (B,T,H,D) dtype (normally qn, kn from rope_qknorm_fwd), read.
  *   ve, gate: both NULL, or ve (B,T,H*D) dtype and gate (B,T,H) float, read.
+ *   ve_ids, ve_rows: NULL and 0, or the value-embedding table mode (lanjinlin.com.cn repost,
+ *   "3. Value Embeddings": the per-layer value embedding is a lookup of the token ids): ve is
+ *   then a (ve_rows, H*D) dtype table and token (b,t) uses row ve_ids[b*T + t] (device (B,T)
+ *   int32, read), gathered inside the kernels' V-row loads; an id outside [0, ve_rows) reads
+ *   as a zero row. Needs ve and gate.
  *   o  : device (B,T,H,D) dtype, written.     lse: device (B,H,T) float, natural log, written.
  *   doc_bounds: NULL, or swa_doc_bounds' output for this batch: then a token also sees only
  *   keys of its own document (j >= start of i's run), on top of the causal window.
  *   scale: finite, > 0 (1/sqrt(D) for this model).
  */
 int swa_fwd(const void* q, const void* k, const void* v, const void* ve, const float* gate,
-            const int* doc_bounds, void* o, float* lse, int B, int T, int H, int D, int window,
-            float scale, swa_dtype dtype, void* stream);
+            const int* ve_ids, int ve_rows, const int* doc_bounds, void* o, float* lse, int B,
+            int T, int H, int D, int window, float scale, swa_dtype dtype, void* stream);
 
 /* Bytes of workspace swa_bwd needs: the row terms -delta and -lse*log2(e), each (B,H,T) float32,
  * 256-byte aligned inside the block and followed by 512 bytes of slack. */
@@ -160,17 +166,22 @@ size_t swa_bwd_workspace_size(int B, int T, int H, int D, swa_dtype dtype);
  *   P = exp(s - lse); dv_eff = P^T dO; dP = dO v_eff^T; delta_i = dO_i . O_i;
  *   dS = P * (dP - delta); dq = scale dS k; dk = scale dS^T q. Outputs are bitwise repeatable.
  *   With the gate: dv = dv_eff, dve = gate * dv_eff, dgate = sum_d dv_eff * ve.
- *   q, k, v, ve, gate, doc_bounds: as given to swa_fwd.  o, lse: swa_fwd's outputs.
- *   dO: (B,T,H,D) dtype.
+ *   q, k, v, ve, gate, ve_ids, ve_rows, doc_bounds: as given to swa_fwd.
+ *   o, lse: swa_fwd's outputs.   dO: (B,T,H,D) dtype.
  *   dq, dk, dv: device (B,T,H,D) dtype, written.
  *   dve (B,T,H*D) dtype and dgate (B,T,H) float: written when the gate is used (both
  *   required then), must be NULL otherwise.
+ *   In the table mode dve is instead the table's gradient, a (ve_rows, H*D) FLOAT array that
+ *   is ACCUMULATED into (sum over the tokens of each id of gate * dv_eff, float atomics):
+ *   the caller zeroes it (or passes a running gradient), and its bits depend on the order of
+ *   the atomics (every other output stays bitwise repeatable). dgate uses the table row.
  *   workspace: device, >= swa_bwd_workspace_size() bytes, 256-byte aligned, clobbered.
  */
 int swa_bwd(const void* q, const void* k, const void* v, const void* ve, const float* gate,
-            const int* doc_bounds, const void* o, const float* lse, const void* dO, void* dq,
-            void* dk, void* dv, void* dve, float* dgate, void* workspace, size_t ws_bytes, int B,
-            int T, int H, int D, int window, float scale, swa_dtype dtype, void* stream);
+            const int* ve_ids, int ve_rows, const int* doc_bounds, const void* o, const float* lse,
+            const void* dO, void* dq, void* dk, void* dv, void* dve, float* dgate, void* workspace,
+            size_t ws_bytes, int B, int T, int H, int D, int window, float scale, swa_dtype dtype,
+            void* stream);
 
 /*
  * The three stages swa_bwd runs, for callers that schedule or time them separately. Call them
@@ -188,9 +199,10 @@ int swa_bwd_preprocess(const void* o, const void* dO, const float* lse, void* wo
  *   filled by swa_bwd_preprocess.
  */
 int swa_bwd_dkdv(const void* q, const void* k, const void* v, const void* ve, const float* gate,
-                 const int* doc_bounds, const float* lse, const void* dO, void* dk, void* dv,
-                 void* dve, float* dgate, void* workspace, size_t ws_bytes, int B, int T, int H,
-                 int D, int window, float scale, swa_dtype dtype, void* stream);
+                 const int* ve_ids, int ve_rows, const int* doc_bounds, const float* lse,
+                 const void* dO, void* dk, void* dv, void* dve, float* dgate, void* workspace,
+                 size_t ws_bytes, int B, int T, int H, int D, int window, float scale,
+                 swa_dtype dtype, void* stream);
 
 /*
  * swa_bwd_dq — the query-block-major part: recomputes the scores per query block and writes
@@ -198,9 +210,9 @@ int swa_bwd_dkdv(const void* q, const void* k, const void* v, const void* ve, co
  *   swa_bwd_preprocess. May run before, after or concurrently with swa_bwd_dkdv.
  */
 int swa_bwd_dq(const void* q, const void* k, const void* v, const void* ve, const float* gate,
-               const int* doc_bounds, const float* lse, const void* dO, void* dq, void* workspace,
-               size_t ws_bytes, int B, int T, int H, int D, int window, float scale,
-               swa_dtype dtype, void* stream);
+               const int* ve_ids, int ve_rows, const int* doc_bounds, const float* lse,
+               const void* dO, void* dq, void* workspace, size_t ws_bytes, int B, int T, int H,
+               int D, int window, float scale, swa_dtype dtype, void* stream);
 
 /*
  * Sliding-window decoding from a K/V cache ("GPT-2 124M 复现" §7: generation that keeps the

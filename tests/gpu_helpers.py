@@ -74,20 +74,25 @@ def gpu_layer(x: dict, wl, window: int):
     cs = sw.rope_table(wl.T, wl.D, wl.base)
     qn, kn = sw.rope_qknorm_fwd(q, k, cs, wl.eps)
     out = {"qn": qn, "kn": kn}
-    ve = gate = None
+    ve = gate = ve_ids = None
     if wl.gate:
         xg = dev(x["x"], dt)
         Wg = torch.from_numpy(x["Wg"]).cuda()
-        ve = dev(x["ve"], dt)
+        if "table" in x:   # table mode: the kernels gather the rows by token id
+            ve = dev(x["table"], dt)
+            ve_ids = torch.from_numpy(x["ids"].astype(np.int32)).cuda()
+        else:
+            ve = dev(x["ve"], dt)
         gate = sw.ve_gate_v(xg, Wg)
         out["gate"] = gate
     bounds = None
     if "doc_id" in x:
         bounds = sw.swa_doc_bounds(torch.from_numpy(x["doc_id"].astype(np.int32)).cuda())
         out["doc_bounds"] = bounds
-    o, lse = sw.swa_fwd(qn, kn, v, window, wl.scale, ve=ve, gate=gate, doc_bounds=bounds)
+    o, lse = sw.swa_fwd(qn, kn, v, window, wl.scale, ve=ve, gate=gate, doc_bounds=bounds,
+                        ve_ids=ve_ids)
     grads = sw.swa_bwd(qn, kn, v, o, lse, dO, window, wl.scale, ve=ve, gate=gate,
-                       doc_bounds=bounds)
+                       doc_bounds=bounds, ve_ids=ve_ids)
     dqn, dkn, dv = grads[:3]
     dq, dk = sw.rope_qknorm_bwd(q, k, cs, dqn, dkn, wl.eps)
     out.update(O=o, lse=lse, dqh=dqn, dkh=dkn, dv=dv, dq=dq, dk=dk)
@@ -105,9 +110,11 @@ def oracle_layer(x: dict, wl, window: int, sel=None):
     kw = dict(base=wl.base, eps=wl.eps, scale=wl.scale)
     gk = {}
     if wl.gate:
-        B, T = wl.B, wl.T
-        gk = dict(x32=x["x"][..., :32].astype(np.float64), Wg=x["Wg"].astype(np.float64),
-                  ve=x["ve"].astype(np.float64))
+        if "table" in x:
+            ve = oracle.ve_lookup(x["table"].astype(np.float64), x["ids"])
+        else:
+            ve = x["ve"].astype(np.float64)
+        gk = dict(x32=x["x"][..., :32].astype(np.float64), Wg=x["Wg"].astype(np.float64), ve=ve)
     doc = x.get("doc_id")
     if sel is not None:
         b, h = sel
@@ -120,6 +127,8 @@ def oracle_layer(x: dict, wl, window: int, sel=None):
     fwd = oracle.layer_fwd(f["q"], f["k"], f["v"], window, round_boundary=(wl.dtype == "bf16"),
                            doc_id=doc, **kw, **gk)
     bwd = oracle.layer_bwd(f["q"], f["k"], f["v"], f["dO"], window, fwd, doc_id=doc, **kw, **gk)
+    if wl.gate and "table" in x and sel is None:
+        bwd["dtable"] = oracle.ve_table_grad(bwd["dve"], x["ids"], x["table"].shape[0])
     return fwd, bwd
 
 
@@ -147,6 +156,10 @@ def compare_layer(g: dict, fwd: dict, bwd: dict, dtype: str, sel=None, gate=Fals
         errs["gate"] = check("gate", pick("gate", g["gate"], "bth"), fwd["g"], "f32")
         if sel is None:
             B, T, H, D = g["O"].shape
-            errs["dve"] = check("dve", host(g["dve"]), bwd["dve"], dtype)
+            if "dtable" in bwd:   # a float sum over the tokens of each id
+                errs["dtable"] = check("dtable", host(g["dve"]), bwd["dtable"], dtype,
+                                       sum_scaled=True)
+            else:
+                errs["dve"] = check("dve", host(g["dve"]), bwd["dve"], dtype)
             errs["dgate"] = check("dgate", host(g["dgate"]), bwd["dg"], dtype, sum_scaled=True)
     return errs

@@ -85,8 +85,8 @@ def test_binding_signatures_match_the_header():
 
 
 def _fwd(lib, q=P, k=P, v=P, ve=None, gate=None, o=P, lse=P, B=1, T=8, H=1, D=64, W=4, scale=0.125,
-         dt=1, doc=None):
-    return lib.swa_fwd(q, k, v, ve, gate, doc, o, lse, B, T, H, D, W, scale, dt, None)
+         dt=1, doc=None, ids=None, rows=0):
+    return lib.swa_fwd(q, k, v, ve, gate, ids, rows, doc, o, lse, B, T, H, D, W, scale, dt, None)
 
 
 def test_swa_fwd_validation(lib):
@@ -105,6 +105,11 @@ def test_swa_fwd_validation(lib):
     assert _fwd(lib, gate=P) == INVALID        # gate without ve
     assert _fwd(lib, B=1 << 20, T=1 << 12, H=1 << 4, D=128) == UNSUPPORTED
     assert _fwd(lib, doc=MIS) == ALIGN                     # document bounds misaligned
+    # value-embedding table mode: ids need the gate, a positive row count, and rows need ids
+    assert _fwd(lib, ids=P, rows=4) == INVALID
+    assert _fwd(lib, ve=P, gate=P, ids=P, rows=0) == INVALID
+    assert _fwd(lib, ve=P, gate=P, rows=3) == INVALID
+    assert _fwd(lib, ve=P, gate=P, ids=P, rows=1 << 30, H=1 << 4, D=128) == UNSUPPORTED
 
 
 def test_doc_bounds_validation(lib):
@@ -120,9 +125,10 @@ def test_swa_bwd_validation(lib):
     assert ws_need >= 2 * (2 * 64 * 3 * 4)          # delta and lse*log2(e), float32 each
     assert lib.swa_bwd_workspace_size(2, 64, 3, 96, 1) == 0
 
-    def bwd(ws=P, ws_bytes=ws_need, ve=None, gate=None, dve=None, dgate=None, W=8, dO=P):
-        return lib.swa_bwd(P, P, P, ve, gate, None, P, P, dO, P, P, P, dve, dgate, ws, ws_bytes, 2, 64, 3,
-                           64, W, 0.125, 1, None)
+    def bwd(ws=P, ws_bytes=ws_need, ve=None, gate=None, dve=None, dgate=None, W=8, dO=P, ids=None,
+            rows=0):
+        return lib.swa_bwd(P, P, P, ve, gate, ids, rows, None, P, P, dO, P, P, P, dve, dgate, ws,
+                           ws_bytes, 2, 64, 3, 64, W, 0.125, 1, None)
 
     assert bwd(ws=None) == WORKSPACE
     assert bwd(ws_bytes=ws_need - 1) == WORKSPACE
@@ -131,20 +137,23 @@ def test_swa_bwd_validation(lib):
     assert bwd(dve=P, dgate=P) == INVALID               # dve/dgate without gate
     assert bwd(W=0) == INVALID
     assert bwd(dO=None) == INVALID
+    assert bwd(ids=P, rows=5) == INVALID                 # table ids without the gate
+    assert bwd(ve=P, gate=P, dve=P, dgate=P, ids=P, rows=-1) == INVALID
 
     # the two compute stages check the same arguments
     def dkdv(ws=P, ws_bytes=ws_need, W=8):
-        return lib.swa_bwd_dkdv(P, P, P, None, None, None, P, P, P, P, None, None, ws, ws_bytes, 2, 64, 3,
-                                64, W, 0.125, 1, None)
+        return lib.swa_bwd_dkdv(P, P, P, None, None, None, 0, None, P, P, P, P, None, None, ws,
+                                ws_bytes, 2, 64, 3, 64, W, 0.125, 1, None)
 
-    def dq(ws=P, ws_bytes=ws_need, W=8, ve=None, gate=None):
-        return lib.swa_bwd_dq(P, P, P, ve, gate, None, P, P, P, ws, ws_bytes, 2, 64, 3, 64, W, 0.125, 1,
-                              None)
+    def dq(ws=P, ws_bytes=ws_need, W=8, ve=None, gate=None, ids=None, rows=0):
+        return lib.swa_bwd_dq(P, P, P, ve, gate, ids, rows, None, P, P, P, ws, ws_bytes, 2, 64, 3, 64,
+                              W, 0.125, 1, None)
 
     assert dkdv(ws=None) == WORKSPACE and dq(ws=None) == WORKSPACE
     assert dkdv(ws_bytes=ws_need - 1) == WORKSPACE and dq(ws_bytes=ws_need - 1) == WORKSPACE
     assert dkdv(W=0) == INVALID and dq(W=0) == INVALID
     assert dq(ve=P) == INVALID                          # ve without gate
+    assert dq(ve=P, gate=P, ids=P, rows=0) == INVALID   # table mode without rows
 
 
 def test_prologue_and_gate_validation(lib):
