@@ -103,6 +103,7 @@ def make_layers(cfg, torch, seed0=1000):
                 t["ve"] = table[ids].contiguous()
             del table
             t["gate"] = torch.empty((B, T, H), dtype=torch.float32, device="cuda")
+            t["veff"] = torch.empty_like(t["v"])   # materialised v + gate * ve, kept for the bwd
         t["W"] = W
         layers.append(t)
     return layers
@@ -138,6 +139,9 @@ def run_bench(args):
         g["dWg"] = torch.empty((32, H), dtype=torch.float32, device="cuda")
     ws = torch.empty(sw.swa_bwd_workspace_size(B, T, H, D, torch.bfloat16), dtype=torch.uint8,
                      device="cuda")
+    if cfg["gate"]:
+        g["gws"] = torch.empty(sw.load().ve_gate_v_bwd_workspace_size(B, T, H), dtype=torch.uint8,
+                               device="cuda")
     lib = sw.load()
     stream = sw._stream()
     P = sw._ptr
@@ -149,6 +153,8 @@ def run_bench(args):
         if st != 0:
             raise sw.SwaError(name, st, lib.swa_last_error().decode())
 
+    fused_gate = args.fused_gate
+
     def step(rec):
         # forward, layers in order
         for li, t in enumerate(layers):
@@ -156,13 +162,18 @@ def run_bench(args):
             rows = 0 if ids is None else t["ve"].shape[0]
             call("rope_qknorm_fwd", P(t["q"]), P(t["k"]), P(cs), P(t["qn"]), P(t["kn"]), B, T, H, D,
                  1e-6, sw.SWA_BF16, stream)
-            ve = gate = None
-            if cfg["gate"]:
-                call("ve_gate_v", P(t["x"]), 1536, P(t["Wg"]), P(t["gate"]), None, None, None, B, T,
-                     H, D, sw.SWA_BF16, stream)
-                ve, gate = t["ve"], t["gate"]
+            ve = gate = fids = None
+            frows, v = 0, t["v"]
+            if cfg["gate"] and fused_gate:
+                call("ve_gate_v", P(t["x"]), 1536, P(t["Wg"]), P(t["gate"]), None, None, None, 0,
+                     None, B, T, H, D, sw.SWA_BF16, stream)
+                ve, gate, fids, frows = t["ve"], t["gate"], ids, rows
+            elif cfg["gate"]:
+                call("ve_gate_v", P(t["x"]), 1536, P(t["Wg"]), P(t["gate"]), P(t["v"]), P(t["ve"]),
+                     P(ids), rows, P(t["veff"]), B, T, H, D, sw.SWA_BF16, stream)
+                v = t["veff"]
             if rec: rec["fwd"][li][0].record()
-            call("swa_fwd", P(t["qn"]), P(t["kn"]), P(t["v"]), P(ve), P(gate), P(ids), rows,
+            call("swa_fwd", P(t["qn"]), P(t["kn"]), P(v), P(ve), P(gate), P(fids), frows,
                  P(bounds), P(t["o"]), P(t["lse"]),
                  B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
             if rec: rec["fwd"][li][1].record()
@@ -171,19 +182,23 @@ def run_bench(args):
             t = layers[li]
             bounds, ids = t.get("bounds"), t.get("ids")
             rows = 0 if ids is None else t["ve"].shape[0]
-            ve = gate = dve = dgate = None
-            if cfg["gate"]:
+            ve = gate = dve = dgate = fids = None
+            frows, v = 0, t["v"]
+            if cfg["gate"] and fused_gate:
                 ve, gate, dve, dgate = t["ve"], t["gate"], g["dve"], g["dgate"]
+                fids, frows = ids, rows
+            elif cfg["gate"]:
+                v = t["veff"]
             if rec: rec["bwd"][li][0].record()
             call("swa_bwd_preprocess", P(t["o"]), P(t["dO"]), P(t["lse"]), P(ws), nws, B, T, H, D,
                  sw.SWA_BF16, stream)
             if rec: rec["bwd"][li][1].record()
-            call("swa_bwd_dkdv", P(t["qn"]), P(t["kn"]), P(t["v"]), P(ve), P(gate), P(ids), rows,
+            call("swa_bwd_dkdv", P(t["qn"]), P(t["kn"]), P(v), P(ve), P(gate), P(fids), frows,
                  P(bounds), P(t["lse"]),
                  P(t["dO"]), P(g["dkn"]), P(g["dv"]), P(dve), P(dgate), P(ws), nws,
                  B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
             if rec: rec["bwd"][li][2].record()
-            call("swa_bwd_dq", P(t["qn"]), P(t["kn"]), P(t["v"]), P(ve), P(gate), P(ids), rows,
+            call("swa_bwd_dq", P(t["qn"]), P(t["kn"]), P(v), P(ve), P(gate), P(fids), frows,
                  P(bounds), P(t["lse"]),
                  P(t["dO"]), P(g["dqn"]), P(ws), nws, B, T, H, D, t["W"], scale, sw.SWA_BF16,
                  stream)
@@ -191,8 +206,12 @@ def run_bench(args):
             call("rope_qknorm_bwd", P(t["q"]), P(t["k"]), P(cs), P(g["dqn"]), P(g["dkn"]), P(g["dq"]),
                  P(g["dk"]), B, T, H, D, 1e-6, sw.SWA_BF16, stream)
             if cfg["gate"]:
-                call("ve_gate_v_bwd", P(t["x"]), 1536, P(t["Wg"]), P(gate), P(dgate), P(g["dWg"]),
-                     None, B, T, H, sw.SWA_BF16, stream)
+                if not fused_gate:   # dve, dgate from dv_eff (= dv)
+                    call("ve_gate_dv", P(g["dv"]), P(t["ve"]), P(ids), rows, P(t["gate"]),
+                         P(g["dve"]), P(g["dgate"]), B, T, H, D, sw.SWA_BF16, stream)
+                call("ve_gate_v_bwd", P(t["x"]), 1536, P(t["Wg"]), P(t["gate"]), P(g["dgate"]),
+                     P(g["dWg"]), None, P(g["gws"]), g["gws"].numel(), B, T, H, sw.SWA_BF16,
+                     stream)
 
     for _ in range(args.warmup):
         step(None)
@@ -242,6 +261,9 @@ def run_bench(args):
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "avg_launch_us": round(dom_ms * 1e3, 2),
                 "traffic": traffic_from_profile(dom, args.workload)}
+    if cfg["gate"]:
+        cfg["desc"] += ("; gate fused into the attention kernels" if args.fused_gate
+                        else "; v_eff materialised once per layer")
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
@@ -327,6 +349,8 @@ def run_decode_bench(args):
         st = getattr(lib, name)(*a)
         if st != 0:
             raise sw.SwaError(name, st, lib.swa_last_error().decode())
+
+    fused_gate = args.fused_gate
 
     def step(rec):
         for li, t in enumerate(layers):
@@ -475,6 +499,9 @@ def main():
                     choices=["sssl24", "d24_short", "d24_full", "gpt2_124m", "d24_short_ve",
                              "d24_short_doc", "d24_short_vetable", "d24_decode"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--fused-gate", action="store_true",
+                    help="gated workloads: form v_eff inside the attention kernels instead of "
+                         "materialising it once per layer (the default, faster route)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="only run a plain device-to-device copy of this many MiB 5 times (used to "

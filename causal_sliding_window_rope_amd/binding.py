@@ -30,8 +30,10 @@ SIGNATURES = {
     "rope_table": (_I, [_P, _I, _I, _D, _P]),
     "rope_qknorm_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "rope_qknorm_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
-    "ve_gate_v": (_I, [_P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
-    "ve_gate_v_bwd": (_I, [_P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "ve_gate_v": (_I, [_P, _I, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _P]),
+    "ve_gate_dv": (_I, [_P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "ve_gate_v_bwd_workspace_size": (_S, [_I, _I, _I]),
+    "ve_gate_v_bwd": (_I, [_P, _I, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _P]),
     "swa_doc_bounds": (_I, [_P, _P, _I, _I, _P]),
     "swa_fwd": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "swa_bwd_workspace_size": (_S, [_I, _I, _I, _I, _I]),
@@ -138,18 +140,54 @@ def rope_qknorm_bwd(q, k, cos_sin, dqn, dkn, eps: float = 1e-6):
     return dq, dk
 
 
-def ve_gate_v(x, Wg, v=None, ve=None, materialize: bool = False):
-    """gate (B, T, H) float32; with materialize=True also v_eff = v + gate * ve."""
+def ve_gate_v(x, Wg, v=None, ve=None, materialize: bool = False, ve_ids=None):
+    """gate (B, T, H) float32; with materialize=True also v_eff = v + gate * ve (ve_ids (B, T)
+    int32: ve is a (rows, H*D) table read by token id)."""
     B, T, C = x.shape
     H = Wg.shape[1]
     _check(x, "x")
     _check(Wg, "Wg", (32, H), torch.float32)
     gate = torch.empty((B, T, H), dtype=torch.float32, device=x.device)
     D = v.shape[-1] if v is not None else 64
+    ids, rows = None, 0
+    if materialize:
+        _check(v, "v", (B, T, H, D), x.dtype)
+        if ve_ids is not None:
+            _check(ve_ids, "ve_ids", (B, T), torch.int32)
+            _check(ve, "ve", (ve.shape[0], H * D), x.dtype)
+            ids, rows = _ptr(ve_ids), ve.shape[0]
+        else:
+            _check(ve, "ve", (B, T, H * D), x.dtype)
     v_eff = torch.empty_like(v) if materialize else None
     _call("ve_gate_v", _ptr(x), C, _ptr(Wg), _ptr(gate), _ptr(v if materialize else None),
-          _ptr(ve if materialize else None), _ptr(v_eff), B, T, H, D, _dt(x), _stream())
+          _ptr(ve if materialize else None), ids, rows, _ptr(v_eff), B, T, H, D, _dt(x),
+          _stream())
     return (gate, v_eff) if materialize else gate
+
+
+def ve_gate_dv(dv_eff, ve, gate, ve_ids=None, dve=None):
+    """(dve, dgate) from dv_eff. Per-token mode: dve (B, T, H*D) in dv_eff's dtype. Table mode
+    (ve_ids): dve is the (rows, H*D) float table gradient, accumulated into (zeroed if new)."""
+    B, T, H, D = dv_eff.shape
+    _check(dv_eff, "dv_eff")
+    _check(gate, "gate", (B, T, H), torch.float32)
+    ids, rows = None, 0
+    if ve_ids is not None:
+        _check(ve_ids, "ve_ids", (B, T), torch.int32)
+        _check(ve, "ve", (ve.shape[0], H * D), dv_eff.dtype)
+        ids, rows = _ptr(ve_ids), ve.shape[0]
+        if dve is None:
+            dve = torch.zeros((rows, H * D), dtype=torch.float32, device=dv_eff.device)
+        _check(dve, "dve", (rows, H * D), torch.float32)
+    else:
+        _check(ve, "ve", (B, T, H * D), dv_eff.dtype)
+        if dve is None:
+            dve = torch.empty((B, T, H * D), dtype=dv_eff.dtype, device=dv_eff.device)
+        _check(dve, "dve", (B, T, H * D), dv_eff.dtype)
+    dgate = torch.empty((B, T, H), dtype=torch.float32, device=dv_eff.device)
+    _call("ve_gate_dv", _ptr(dv_eff), _ptr(ve), ids, rows, _ptr(gate), _ptr(dve), _ptr(dgate),
+          B, T, H, D, _dt(dv_eff), _stream())
+    return dve, dgate
 
 
 def ve_gate_v_bwd(x, Wg, gate, dgate, want_dx32: bool = True):
@@ -160,8 +198,10 @@ def ve_gate_v_bwd(x, Wg, gate, dgate, want_dx32: bool = True):
     _check(dgate, "dgate", (B, T, H), torch.float32)
     dWg = torch.empty((32, H), dtype=torch.float32, device=x.device)
     dx32 = torch.empty((B, T, 32), dtype=x.dtype, device=x.device) if want_dx32 else None
+    nws = load().ve_gate_v_bwd_workspace_size(B, T, H)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=x.device)
     _call("ve_gate_v_bwd", _ptr(x), C, _ptr(Wg), _ptr(gate), _ptr(dgate), _ptr(dWg), _ptr(dx32),
-          B, T, H, _dt(x), _stream())
+          _ptr(ws), nws, B, T, H, _dt(x), _stream())
     return dWg, dx32
 
 

@@ -135,8 +135,21 @@ int rope_qknorm_bwd(const void* q, const void* k, const float* cos_sin, const vo
                                                 dtype == SWA_BF16, (hipStream_t)stream), fn);
 }
 
+// Value-embedding table mode arguments of the gate calls (no AttnShape there).
+static int check_ve_ids(const char* fn, const int* ve_ids, int ve_rows, int H, int D) {
+  if (!ve_ids) {
+    if (ve_rows != 0) return fail(SWA_ERR_INVALID_ARG, "%s: ve_rows must be 0 without ve_ids", fn);
+    return ok();
+  }
+  if (ve_rows < 1) return fail(SWA_ERR_INVALID_ARG, "%s: ve_rows must be >= 1 with ve_ids", fn);
+  if ((long long)ve_rows * H * D >= (1LL << 40))
+    return fail(SWA_ERR_UNSUPPORTED, "%s: value-embedding table too large", fn);
+  return ok();
+}
+
 int ve_gate_v(const void* x, int ldx, const float* Wg, float* gate, const void* v, const void* ve,
-              void* v_eff, int B, int T, int H, int D, swa_dtype dtype, void* stream) {
+              const int* ve_ids, int ve_rows, void* v_eff, int B, int T, int H, int D,
+              swa_dtype dtype, void* stream) {
   const char* fn = "ve_gate_v";
   SWA_TRY(check_shape(fn, B, T, H, D, dtype));
   if (!x || !Wg || !gate) return fail(SWA_ERR_INVALID_ARG, "%s: x, Wg and gate are required", fn);
@@ -144,19 +157,51 @@ int ve_gate_v(const void* x, int ldx, const float* Wg, float* gate, const void* 
   const int nset = (v != nullptr) + (ve != nullptr) + (v_eff != nullptr);
   if (nset != 0 && nset != 3)
     return fail(SWA_ERR_INVALID_ARG, "%s: v, ve, v_eff must be all set or all NULL", fn);
-  if (nset == 3) { SWA_TRY(need(fn, "v", v)); SWA_TRY(need(fn, "ve", ve)); SWA_TRY(need(fn, "v_eff", v_eff)); }
-  return hip_status(swa::launch_ve_gate(x, ldx, Wg, gate, v, ve, v_eff, B, T, H, D,
-                                        dtype == SWA_BF16, (hipStream_t)stream), fn);
+  if (nset == 3) {
+    SWA_TRY(need(fn, "v", v)); SWA_TRY(need(fn, "ve", ve)); SWA_TRY(need(fn, "v_eff", v_eff));
+  }
+  if (ve_ids && nset == 0)
+    return fail(SWA_ERR_INVALID_ARG, "%s: ve_ids needs v, ve and v_eff", fn);
+  SWA_TRY(check_ve_ids(fn, ve_ids, ve_rows, H, D));
+  return hip_status(swa::launch_ve_gate(x, ldx, Wg, gate, v, ve, ve_ids, ve_rows, v_eff, B, T, H,
+                                        D, dtype == SWA_BF16, (hipStream_t)stream), fn);
+}
+
+int ve_gate_dv(const void* dv_eff, const void* ve, const int* ve_ids, int ve_rows,
+               const float* gate, void* dve, float* dgate, int B, int T, int H, int D,
+               swa_dtype dtype, void* stream) {
+  const char* fn = "ve_gate_dv";
+  SWA_TRY(check_shape(fn, B, T, H, D, dtype));
+  SWA_TRY(need(fn, "dv_eff", dv_eff)); SWA_TRY(need(fn, "ve", ve));
+  SWA_TRY(need(fn, "gate", gate)); SWA_TRY(need(fn, "dve", dve));
+  SWA_TRY(need(fn, "dgate", dgate));
+  SWA_TRY(check_ve_ids(fn, ve_ids, ve_rows, H, D));
+  return hip_status(swa::launch_ve_gate_dv(dv_eff, ve, ve_ids, ve_rows, gate, dve, dgate, B, T, H,
+                                           D, dtype == SWA_BF16, (hipStream_t)stream), fn);
+}
+
+size_t ve_gate_v_bwd_workspace_size(int B, int T, int H) {
+  if (B < 1 || T < 1 || H < 1 || H > SWA_GATE_MAX_HEADS) return 0;
+  return swa::gate_bwd_workspace_bytes(B, T, H);
 }
 
 int ve_gate_v_bwd(const void* x, int ldx, const float* Wg, const float* gate, const float* dgate,
-                  float* dWg, void* dx32, int B, int T, int H, swa_dtype dtype, void* stream) {
+                  float* dWg, void* dx32, void* workspace, size_t ws_bytes, int B, int T, int H,
+                  swa_dtype dtype, void* stream) {
   const char* fn = "ve_gate_v_bwd";
   SWA_TRY(check_shape(fn, B, T, H, 64, dtype));
   if (!x || !Wg || !gate || !dgate || !dWg)
     return fail(SWA_ERR_INVALID_ARG, "%s: x, Wg, gate, dgate and dWg are required", fn);
   if (ldx < SWA_GATE_CHANNELS) return fail(SWA_ERR_INVALID_ARG, "%s: ldx must be >= 32", fn);
-  return hip_status(swa::launch_ve_gate_bwd(x, ldx, Wg, gate, dgate, dWg, dx32, B, T, H,
+  if (H > SWA_GATE_MAX_HEADS)
+    return fail(SWA_ERR_UNSUPPORTED, "%s: at most %d heads", fn, SWA_GATE_MAX_HEADS);
+  if (!workspace) return fail(SWA_ERR_WORKSPACE, "%s: workspace is required", fn);
+  if (!aligned16(workspace))
+    return fail(SWA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  if (ws_bytes < swa::gate_bwd_workspace_bytes(B, T, H))
+    return fail(SWA_ERR_WORKSPACE, "%s: workspace of %zu bytes is smaller than the %zu needed", fn,
+                ws_bytes, swa::gate_bwd_workspace_bytes(B, T, H));
+  return hip_status(swa::launch_ve_gate_bwd(x, ldx, Wg, gate, dgate, dWg, dx32, workspace, B, T, H,
                                             dtype == SWA_BF16, (hipStream_t)stream), fn);
 }
 
@@ -180,9 +225,7 @@ static int check_ve_table(const char* fn, const void* ve, const int* ve_ids, int
     return ok();
   }
   if (!ve) return fail(SWA_ERR_INVALID_ARG, "%s: ve_ids needs ve and gate", fn);
-  if (ve_rows < 1) return fail(SWA_ERR_INVALID_ARG, "%s: ve_rows must be >= 1 with ve_ids", fn);
-  if ((long long)ve_rows * H * D >= (1LL << 40))
-    return fail(SWA_ERR_UNSUPPORTED, "%s: value-embedding table too large", fn);
+  SWA_TRY(check_ve_ids(fn, ve_ids, ve_rows, H, D));
   a->ve_ids = ve_ids;
   a->ve_rows = ve_rows;
   return ok();

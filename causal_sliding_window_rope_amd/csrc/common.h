@@ -36,6 +36,24 @@ __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// A 128-bit word as float values: 4 float or 8 bf16 elements (overloaded on the array size).
+__device__ __forceinline__ void unpack16(uint4 w, float (&o)[4]) {
+  o[0] = __uint_as_float(w.x); o[1] = __uint_as_float(w.y);
+  o[2] = __uint_as_float(w.z); o[3] = __uint_as_float(w.w);
+}
+__device__ __forceinline__ void unpack16(uint4 w, float (&o)[8]) {
+  o[0] = bf_lo(w.x); o[1] = bf_hi(w.x); o[2] = bf_lo(w.y); o[3] = bf_hi(w.y);
+  o[4] = bf_lo(w.z); o[5] = bf_hi(w.z); o[6] = bf_lo(w.w); o[7] = bf_hi(w.w);
+}
+__device__ __forceinline__ uint4 pack16(const float (&v)[4]) {
+  return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                    __float_as_uint(v[3]));
+}
+__device__ __forceinline__ uint4 pack16(const float (&v)[8]) {
+  return make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]),
+                    pack_bf2(v[6], v[7]));
+}
+
 // Wave64 cross-lane helpers.
 __device__ __forceinline__ float xor_shfl(float v, int mask) { return __shfl_xor(v, mask, 64); }
 

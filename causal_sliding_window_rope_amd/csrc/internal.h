@@ -27,11 +27,15 @@ hipError_t launch_rope_qknorm_bwd(const void* q, const void* k, const float* cs,
                                   float eps, bool bf16, hipStream_t s);
 
 hipError_t launch_ve_gate(const void* x, int ldx, const float* Wg, float* gate, const void* v,
-                          const void* ve, void* v_eff, int B, int T, int H, int D, bool bf16,
-                          hipStream_t s);
+                          const void* ve, const int* ids, int ve_rows, void* v_eff, int B, int T,
+                          int H, int D, bool bf16, hipStream_t s);
+hipError_t launch_ve_gate_dv(const void* dv, const void* ve, const int* ids, int ve_rows,
+                             const float* gate, void* dve, float* dgate, int B, int T, int H,
+                             int D, bool bf16, hipStream_t s);
+size_t gate_bwd_workspace_bytes(int B, int T, int H);
 hipError_t launch_ve_gate_bwd(const void* x, int ldx, const float* Wg, const float* gate,
-                              const float* dgate, float* dWg, void* dx32, int B, int T, int H,
-                              bool bf16, hipStream_t s);
+                              const float* dgate, float* dWg, void* dx32, void* ws, int B, int T,
+                              int H, bool bf16, hipStream_t s);
 
 hipError_t launch_fwd(const AttnShape& a, const void* q, const void* k, const void* v,
                       const void* ve, const float* gate, void* o, float* lse, bool bf16,

@@ -37,7 +37,7 @@
  *     launch failed) and swa_last_error() describes the problem. No C++ exception crosses
  *     the ABI. Device pointers must be 16-byte aligned (128-bit vector access).
  *   - Gradients are overwritten, never accumulated into (except the value-embedding table
- *     gradient of swa_bwd / swa_bwd_dkdv in the table mode, see there).
+ *     gradient of swa_bwd / swa_bwd_dkdv / ve_gate_dv in the table mode, see there).
  */
 #ifndef SWA_H_
 #define SWA_H_
@@ -61,6 +61,8 @@ typedef enum {
 
 #define SWA_WINDOW_FULL (-1)
 #define SWA_GATE_CHANNELS 32
+/* Most heads ve_gate_v_bwd handles (its LDS staging holds 128 rows of dz per block). */
+#define SWA_GATE_MAX_HEADS 64
 
 /* Text of the last non-zero status returned on the calling thread ("" if none). */
 const char* swa_last_error(void);
@@ -107,25 +109,50 @@ int rope_qknorm_bwd(const void* q, const void* k, const float* cos_sin, const vo
  * ve_gate_v — value-embedding gate (lanjinlin.com.cn repost, "3. Value Embeddings"):
  *   gate[b,t,h] = 2 * sigmoid(sum_{c<32} x[b,t,c] * Wg[c,h])   (range (0, 2)).
  * Optionally materialises v_eff = v + gate * ve (pass v, ve, v_eff all non-NULL, or all
- * NULL). swa_fwd/swa_bwd can instead take (ve, gate) and form v_eff inside their V-tile
- * loads, which is the fused path.
+ * NULL); swa_fwd / swa_bwd then run on v_eff without the gate and ve_gate_dv closes the
+ * backward. This is the faster route on MI355X; swa_fwd / swa_bwd can instead take (ve, gate)
+ * and form v_eff inside their V-tile loads.
  *   x   : device (B,T,ldx) dtype, ldx >= 32 (elements), read.    Wg: device (32,H) float, read.
  *   gate: device (B,T,H) float, written.
+ *   v, ve: (B,T,H,D) and (B,T,H*D) dtype, read.   v_eff: (B,T,H,D) dtype, written.
+ *   ve_ids, ve_rows: NULL and 0, or the table mode as in swa_fwd: ve is a (ve_rows, H*D) table
+ *   and token (b,t) reads row ve_ids[b*T + t] (an id outside [0, ve_rows): zero row).
  */
 int ve_gate_v(const void* x, int ldx, const float* Wg, float* gate, const void* v,
-              const void* ve, void* v_eff, int B, int T, int H, int D, swa_dtype dtype,
-              void* stream);
+              const void* ve, const int* ve_ids, int ve_rows, void* v_eff, int B, int T, int H,
+              int D, swa_dtype dtype, void* stream);
 
 /*
- * ve_gate_v_bwd — backward of the gate given dgate = dL/dgate (B,T,H) float (from swa_bwd):
+ * ve_gate_dv — backward of v_eff = v + gate * ve through ve and the gate, from
+ *   dv_eff = the dv that swa_bwd returns when it ran on a materialised v_eff
+ *   (lanjinlin.com.cn repost, "3. Value Embeddings"; dv itself is dv_eff):
+ *   dve = gate * dv_eff;   dgate[b,t,h] = sum_d dv_eff[b,t,h,d] * ve[b,t,h*D + d].
+ *   dv_eff: (B,T,H,D) dtype, read.  ve: as given to ve_gate_v.  gate: (B,T,H) float, read.
+ *   dve: (B,T,H*D) dtype, written; in the table mode (ve_ids non-NULL) the table's gradient, a
+ *   (ve_rows, H*D) FLOAT array ACCUMULATED into with float atomics (the caller zeroes it; its
+ *   bits depend on the order of the atomics).   dgate: (B,T,H) float, written.
+ */
+int ve_gate_dv(const void* dv_eff, const void* ve, const int* ve_ids, int ve_rows,
+               const float* gate, void* dve, float* dgate, int B, int T, int H, int D,
+               swa_dtype dtype, void* stream);
+
+/* Bytes of workspace ve_gate_v_bwd needs: 32*H float partial sums per chunk of 128 rows of the
+ * B*T rows. 0 for invalid sizes (or H > SWA_GATE_MAX_HEADS). */
+size_t ve_gate_v_bwd_workspace_size(int B, int T, int H);
+
+/*
+ * ve_gate_v_bwd — backward of the gate given dgate = dL/dgate (B,T,H) float (from swa_bwd
+ *   or ve_gate_dv):
  *   dz = dgate * gate * (1 - gate/2);  dWg[c,h] = sum_{b,t} x[b,t,c] dz[b,t,h] (overwritten);
  *   dx32[b,t,c] = sum_h dz[b,t,h] Wg[c,h]   (optional; dx32 NULL skips it).
- * dWg is reduced in a fixed order (bitwise repeatable).
+ * dWg is reduced in two passes with a fixed order (bitwise repeatable): partial sums of each
+ * chunk of 128 rows into the workspace, then the chunks in order. H <= SWA_GATE_MAX_HEADS.
  *   dx32: device (B,T,32) dtype, written.
+ *   workspace: device, >= ve_gate_v_bwd_workspace_size() bytes, 16-byte aligned, clobbered.
  */
 int ve_gate_v_bwd(const void* x, int ldx, const float* Wg, const float* gate,
-                  const float* dgate, float* dWg, void* dx32, int B, int T, int H,
-                  swa_dtype dtype, void* stream);
+                  const float* dgate, float* dWg, void* dx32, void* workspace, size_t ws_bytes,
+                  int B, int T, int H, swa_dtype dtype, void* stream);
 
 /*
  * swa_doc_bounds — document segments of packed rows ("从4万美元到73美元" §6.1: BOS-aligned rows

@@ -67,8 +67,10 @@ def announce(*parts):
     sys.stdout.flush()
 
 
-def gpu_layer(x: dict, wl, window: int):
-    """Whole layer on the GPU: prologue, optional gate, swa_fwd, swa_bwd, prologue backward."""
+def gpu_layer(x: dict, wl, window: int, fused_gate: bool = True):
+    """Whole layer on the GPU: prologue, optional gate, swa_fwd, swa_bwd, prologue backward.
+    fused_gate=False takes the materialised route: ve_gate_v writes v_eff, the attention runs
+    without the gate, ve_gate_dv turns dv_eff into dve and dgate."""
     dt = wl.dtype
     q, k, v, dO = (dev(x[n], dt) for n in ("q", "k", "v", "dO"))
     cs = sw.rope_table(wl.T, wl.D, wl.base)
@@ -83,16 +85,24 @@ def gpu_layer(x: dict, wl, window: int):
             ve_ids = torch.from_numpy(x["ids"].astype(np.int32)).cuda()
         else:
             ve = dev(x["ve"], dt)
-        gate = sw.ve_gate_v(xg, Wg)
+        if fused_gate:
+            gate = sw.ve_gate_v(xg, Wg)
+        else:
+            gate, v = sw.ve_gate_v(xg, Wg, v, ve, materialize=True, ve_ids=ve_ids)
+            ve_kernel = (ve, ve_ids)
+            ve = ve_ids = None
         out["gate"] = gate
     bounds = None
     if "doc_id" in x:
         bounds = sw.swa_doc_bounds(torch.from_numpy(x["doc_id"].astype(np.int32)).cuda())
         out["doc_bounds"] = bounds
-    o, lse = sw.swa_fwd(qn, kn, v, window, wl.scale, ve=ve, gate=gate, doc_bounds=bounds,
+    fgate = gate if ve is not None else None
+    o, lse = sw.swa_fwd(qn, kn, v, window, wl.scale, ve=ve, gate=fgate, doc_bounds=bounds,
                         ve_ids=ve_ids)
-    grads = sw.swa_bwd(qn, kn, v, o, lse, dO, window, wl.scale, ve=ve, gate=gate,
+    grads = sw.swa_bwd(qn, kn, v, o, lse, dO, window, wl.scale, ve=ve, gate=fgate,
                        doc_bounds=bounds, ve_ids=ve_ids)
+    if wl.gate and not fused_gate:
+        grads = tuple(grads) + sw.ve_gate_dv(grads[2], ve_kernel[0], gate, ve_ids=ve_kernel[1])
     dqn, dkn, dv = grads[:3]
     dq, dk = sw.rope_qknorm_bwd(q, k, cs, dqn, dkn, wl.eps)
     out.update(O=o, lse=lse, dqh=dqn, dkh=dkn, dv=dv, dq=dq, dk=dk)

@@ -166,9 +166,25 @@ def test_prologue_and_gate_validation(lib):
     assert lib.rope_qknorm_fwd(P, MIS, P, ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000), 1, 8,
                                1, 64, 1e-6, 1, None) == ALIGN
     assert lib.rope_qknorm_bwd(P, P, P, None, P, P, P, 1, 8, 1, 64, 1e-6, 1, None) == INVALID
-    assert lib.ve_gate_v(P, 16, P, P, None, None, None, 1, 8, 2, 64, 1, None) == INVALID  # ldx < 32
-    assert lib.ve_gate_v(P, 64, P, P, P, None, None, 1, 8, 2, 64, 1, None) == INVALID    # partial
-    assert lib.ve_gate_v_bwd(P, 64, P, P, None, P, None, 1, 8, 2, 1, None) == INVALID
+    assert lib.ve_gate_v(P, 16, P, P, None, None, None, 0, None, 1, 8, 2, 64, 1, None) == INVALID  # ldx
+    assert lib.ve_gate_v(P, 64, P, P, P, None, None, 0, None, 1, 8, 2, 64, 1, None) == INVALID  # partial
+    # table ids without the materialisation, and a table without rows
+    assert lib.ve_gate_v(P, 64, P, P, None, None, P, 4, None, 1, 8, 2, 64, 1, None) == INVALID
+    assert lib.ve_gate_v(P, 64, P, P, P, P, P, 0, P, 1, 8, 2, 64, 1, None) == INVALID
+    assert lib.ve_gate_dv(None, P, None, 0, P, P, P, 1, 8, 2, 64, 1, None) == INVALID
+    assert lib.ve_gate_dv(P, P, None, 0, P, P, None, 1, 8, 2, 64, 1, None) == INVALID   # no dgate
+    assert lib.ve_gate_dv(P, P, None, 3, P, P, P, 1, 8, 2, 64, 1, None) == INVALID      # rows, no ids
+    assert lib.ve_gate_dv(P, P, None, 0, P, P, P, 1, 8, 2, 96, 1, None) == UNSUPPORTED
+    assert lib.ve_gate_dv(P, MIS, None, 0, P, P, P, 1, 8, 2, 64, 1, None) == ALIGN
+    nws = lib.ve_gate_v_bwd_workspace_size(1, 8, 2)
+    assert nws == 32 * 2 * 4                               # one chunk of 128 rows
+    assert lib.ve_gate_v_bwd_workspace_size(1, 300, 3) == 3 * 32 * 3 * 4
+    assert lib.ve_gate_v_bwd_workspace_size(1, 8, 65) == 0
+    assert lib.ve_gate_v_bwd(P, 64, P, P, None, P, None, P, nws, 1, 8, 2, 1, None) == INVALID
+    assert lib.ve_gate_v_bwd(P, 64, P, P, P, P, None, None, nws, 1, 8, 2, 1, None) == WORKSPACE
+    assert lib.ve_gate_v_bwd(P, 64, P, P, P, P, None, P, nws - 4, 1, 8, 2, 1, None) == WORKSPACE
+    assert lib.ve_gate_v_bwd(P, 64, P, P, P, P, None, MIS, nws, 1, 8, 2, 1, None) == ALIGN
+    assert lib.ve_gate_v_bwd(P, 64, P, P, P, P, None, P, nws, 1, 8, 65, 1, None) == UNSUPPORTED
     assert lib.swa_last_error()  # message is set
 
 
