@@ -17,6 +17,7 @@ from .gate import ve_gate, ve_gate_bwd, apply_gate, ve_lookup, ve_table_grad
 from .attention import (window_mask, segment_ids, visible_mask, attention_fwd,
                         attention_fwd_online, attention_bwd, attention_probs, pair_count)
 from .layer import layer_fwd, layer_bwd
+from . import fp8
 
 __all__ = [
     "rope_angles", "rope", "rope_transpose", "rms_norm", "rms_norm_bwd", "rope_qknorm",
@@ -24,5 +25,5 @@ __all__ = [
     "ve_table_grad", "window_mask",
     "segment_ids", "visible_mask",
     "attention_fwd", "attention_fwd_online", "attention_bwd", "attention_probs", "pair_count",
-    "layer_fwd", "layer_bwd",
+    "layer_fwd", "layer_bwd", "fp8",
 ]
