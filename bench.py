@@ -30,6 +30,8 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd+bwd TFLOP/s (unmasked FLOPs) and % of MI355X bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
 PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5033.2       # dense fp8 MFMA: twice the bf16 rate
+FP8_METRIC = "attention forward TFLOP/s on fp8 operands (unmasked FLOPs) and % of MI355X fp8 MFMA peak"
 
 
 def pairs(T: int, W: int) -> int:
@@ -350,8 +352,6 @@ def run_decode_bench(args):
         if st != 0:
             raise sw.SwaError(name, st, lib.swa_last_error().decode())
 
-    fused_gate = args.fused_gate
-
     def step(rec):
         for li, t in enumerate(layers):
             call("swa_decode_prologue", P(t["q"]), P(t["k"]), P(t["v"]), P(cs), cap, P(pos),
@@ -395,6 +395,103 @@ def run_decode_bench(args):
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "avg_launch_us": round(dec_ms / launches * 1e3, 2), "traffic": None},
+    }
+
+
+def run_fp8_bench(args):
+    """The d24 sweep's forward on fp8 operands: for each of the 24 layers (18 with W = 1024,
+    6 with W = 2048; B=16, T=2048, H=12, D=128) rope_qknorm_fwd_fp8 (q_hat, k_hat written as
+    e4m3 at scale 1), swa_fp8_pack of v (scale 1/64) and swa_fwd_fp8. value = 4*D FLOP per
+    visible pair over the 24 layers / step time. The bf16 prologue + swa_fwd on the same inputs
+    are timed alongside (outside the step) for comparison."""
+    import torch
+    from causal_sliding_window_rope_amd import binding as sw
+    lib = sw.load()
+    cfg = layer_list("sssl24")
+    B, T, H, D = cfg["B"], cfg["T"], cfg["H"], cfg["D"]
+    scale = D ** -0.5
+    layers = make_layers(cfg, torch)
+    nv = lib.swa_fp8_v_bytes(B, T, H, D)
+    for t in layers:
+        del t["dO"]
+        t["q8"] = torch.empty((B, T, H, D), dtype=torch.uint8, device="cuda")
+        t["k8"] = torch.empty_like(t["q8"])
+        t["v8t"] = torch.empty(nv, dtype=torch.uint8, device="cuda")
+    cs = sw.rope_table(T, D, 10000.0)
+    P, stream = sw._ptr, sw._stream()
+    sv = 1.0 / 64
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def call(name, *a):
+        st = getattr(lib, name)(*a)
+        if st != 0:
+            raise sw.SwaError(name, st, lib.swa_last_error().decode())
+
+    def step(rec):
+        for li, t in enumerate(layers):
+            call("rope_qknorm_fwd_fp8", P(t["q"]), P(t["k"]), P(cs), P(t["q8"]), P(t["k8"]), B, T,
+                 H, D, 1e-6, sw.SWA_BF16, stream)
+            if rec: rec[li][0].record()
+            call("swa_fp8_pack", None, None, P(t["v"]), 1.0, 1.0, sv, None, None, P(t["v8t"]),
+                 B, T, H, D, sw.SWA_BF16, stream)
+            if rec: rec[li][1].record()
+            call("swa_fwd_fp8", P(t["q8"]), P(t["k8"]), P(t["v8t"]), 1.0, 1.0, sv, None, P(t["o"]),
+                 P(t["lse"]), B, T, H, D, t["W"], scale, stream)
+            if rec: rec[li][2].record()
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    recs = [[[ev(), ev(), ev()] for _ in layers] for _ in range(args.steps)]
+    e0, e1 = ev(), ev()
+    e0.record()
+    for k in range(args.steps):
+        step(recs[k])
+    e1.record()
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / args.steps
+    nl = len(layers)
+    pack_ms = sum(r[l][0].elapsed_time(r[l][1]) for r in recs for l in range(nl)) / args.steps
+    f8_ms = sum(r[l][1].elapsed_time(r[l][2]) for r in recs for l in range(nl)) / args.steps
+    # the bf16 kernel on the same inputs, for comparison
+    for t in layers:
+        call("rope_qknorm_fwd", P(t["q"]), P(t["k"]), P(cs), P(t["qn"]), P(t["kn"]), B, T, H, D,
+             1e-6, sw.SWA_BF16, stream)
+    b16 = [[ev(), ev()] for _ in range(nl * args.steps)]
+    for k in range(args.steps):
+        for li, t in enumerate(layers):
+            b16[k * nl + li][0].record()
+            call("swa_fwd", P(t["qn"]), P(t["kn"]), P(t["v"]), None, None, None, 0, None, P(t["o"]),
+                 P(t["lse"]), B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
+            b16[k * nl + li][1].record()
+    torch.cuda.synchronize()
+    bf_ms = sum(a.elapsed_time(b) for a, b in b16) / args.steps
+    flop = sum(4 * D * pairs(T, t["W"]) * B * H for t in layers)
+    value = flop / (step_ms * 1e-3) / 1e12
+    f8_tf = flop / (f8_ms * 1e-3) / 1e12
+    return {
+        "metric": FP8_METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": "d24 sweep forward on fp8 (e4m3) operands: 24 layers "
+                               "(18 x window 1024, 6 x 2048), B=16, T=2048, H=12, D=128",
+                   "global_batch": B, "seq_len": T, "heads": H, "head_dim": D,
+                   "windows": sorted(set(cfg["windows"])), "parallelism": "single GPU"},
+        "breakdown": {
+            "algorithmic_tflop_per_step": round(flop / 1e12, 4),
+            "swa_fwd_fp8_ms_per_step": round(f8_ms, 4),
+            "swa_fwd_fp8_tflops": round(f8_tf, 2),
+            "swa_fp8_pack_v_ms_per_step": round(pack_ms, 4),
+            "prologue_ms_per_step": round(step_ms - f8_ms - pack_ms, 4),
+            "bf16_swa_fwd_ms_same_inputs": round(bf_ms, 4),
+            "bf16_swa_fwd_tflops": round(flop / (bf_ms * 1e-3) / 1e12, 2),
+        },
+        "roofline": {"bound": "mfma", "kernel": "fwd_fp8_kernel", "achieved": round(f8_tf, 2),
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(f8_tf / PEAK_FP8_TFLOPS, 4),
+                     "avg_launch_us": round(f8_ms / nl * 1e3, 2),
+                     "traffic": traffic_from_profile("fwd_fp8_kernel", "d24_fwd_fp8")},
     }
 
 
@@ -490,6 +587,36 @@ def cpu_baseline_decode(args):
                       f"({tokens:.1f} tokens through 24 layers) in {secs:.1f} s"}
 
 
+def cpu_baseline_fp8(args):
+    """The fp8 oracle (e4m3 quantisation of q_hat, k_hat, v and the float64 attention of the
+    decoded values) on whole (b, h) heads of a short and a full d24 layer, forward only, until
+    about args.cpu_seconds; TFLOP/s with the same 4*D-per-visible-pair count."""
+    import numpy as np
+    from oracle import fp8
+    T, D = 2048, 128
+    rng = np.random.default_rng(77)
+    secs, flop, heads = 0.0, 0, {}
+    while secs < args.cpu_seconds and sum(heads.values()) < 512:
+        W = (1024, 2048)[sum(heads.values()) % 2]
+        q, k, v = (rng.standard_normal((1, T, 1, D)) for _ in range(3))
+        t0 = time.perf_counter()
+        fp8.attention_fwd_fp8(fp8.quantize(q, 1.0), fp8.quantize(k, 1.0), fp8.quantize(v, 1 / 64),
+                              1.0, 1.0, 1 / 64, W, D ** -0.5)
+        secs += time.perf_counter() - t0
+        flop += 4 * D * pairs(T, W)
+        heads[W] = heads.get(W, 0) + 1
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    sample = ", ".join(f"{n} head(s) of window {w}" for w, n in sorted(heads.items()))
+    return {"value": round(flop / secs / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"fp64 numpy fp8 oracle (quantise + forward) on {sample}, T={T}, D={D}; "
+                      f"{secs:.1f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -497,7 +624,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="sssl24",
                     choices=["sssl24", "d24_short", "d24_full", "gpt2_124m", "d24_short_ve",
-                             "d24_short_doc", "d24_short_vetable", "d24_decode"])
+                             "d24_short_doc", "d24_short_vetable", "d24_decode", "d24_fwd_fp8"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--fused-gate", action="store_true",
                     help="gated workloads: form v_eff inside the attention kernels instead of "
@@ -522,6 +649,12 @@ def main():
         print(f"bench.py: --gpus {args.gpus} is not supported; this build measures one GPU "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "d24_fwd_fp8":
+        res = run_fp8_bench(args)
+        if not args.no_cpu_baseline:
+            res["cpu_baseline"] = cpu_baseline_fp8(args)
+        print(json.dumps(res), flush=True)
+        return
     if args.workload == "d24_decode":
         res = run_decode_bench(args)
         if not args.no_cpu_baseline:

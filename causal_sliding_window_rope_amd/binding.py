@@ -44,6 +44,10 @@ SIGNATURES = {
                           _I, _I, _I, _I, _I, _F, _I, _P]),
     "swa_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I,
                         _F, _I, _P]),
+    "swa_fp8_v_bytes": (_S, [_I, _I, _I, _I]),
+    "rope_qknorm_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
+    "swa_fp8_pack": (_I, [_P, _P, _P, _F, _F, _F, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "swa_fwd_fp8": (_I, [_P, _P, _P, _F, _F, _F, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "swa_decode_prologue": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "swa_decode_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "swa_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _F, _I, _P]),
@@ -317,6 +321,57 @@ def swa_bwd_stages(q, k, v, o, lse, dO, window: int, scale: float | None = None,
     if ve is not None:
         return dq, dk, dv, dve, dgate
     return dq, dk, dv
+
+
+def swa_fp8_pack(q=None, k=None, v=None, q_scale: float = 1.0, k_scale: float = 1.0,
+                 v_scale: float = 1.0):
+    """e4m3 codes of q / q_scale, k / k_scale (uint8, (B, T, H, D)) and the packed transposed
+    V operand of v / v_scale (uint8, swa_fp8_v_bytes); None for a tensor not given."""
+    ref = next(t for t in (q, k, v) if t is not None)
+    B, T, H, D = ref.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if t is not None:
+            _check(t, n, (B, T, H, D), ref.dtype)
+    q8 = torch.empty((B, T, H, D), dtype=torch.uint8, device=ref.device) if q is not None else None
+    k8 = torch.empty((B, T, H, D), dtype=torch.uint8, device=ref.device) if k is not None else None
+    v8t = None
+    if v is not None:
+        v8t = torch.empty(load().swa_fp8_v_bytes(B, T, H, D), dtype=torch.uint8, device=ref.device)
+    _call("swa_fp8_pack", _ptr(q), _ptr(k), _ptr(v), float(q_scale), float(k_scale),
+          float(v_scale), _ptr(q8), _ptr(k8), _ptr(v8t), B, T, H, D, _dt(ref), _stream())
+    return q8, k8, v8t
+
+
+def rope_qknorm_fwd_fp8(q, k, cos_sin, eps: float = 1e-6):
+    """q_hat, k_hat as e4m3 codes (uint8, (B, T, H, D), scale 1)."""
+    B, T, H, D = q.shape
+    _check(q, "q", (B, T, H, D))
+    _check(k, "k", (B, T, H, D), q.dtype)
+    _check(cos_sin, "cos_sin", dtype=torch.float32)
+    q8 = torch.empty((B, T, H, D), dtype=torch.uint8, device=q.device)
+    k8 = torch.empty_like(q8)
+    _call("rope_qknorm_fwd_fp8", _ptr(q), _ptr(k), _ptr(cos_sin), _ptr(q8), _ptr(k8), B, T, H, D,
+          float(eps), _dt(q), _stream())
+    return q8, k8
+
+
+def swa_fwd_fp8(q8, k8, v8t, window: int, q_scale: float = 1.0, k_scale: float = 1.0,
+                v_scale: float = 1.0, scale: float | None = None, doc_bounds=None, out=None,
+                lse=None):
+    """Forward on fp8 operands from swa_fp8_pack: O (B, T, H, D) bf16 and lse (B, H, T)."""
+    B, T, H, D = q8.shape
+    _check(q8, "q8", (B, T, H, D), torch.uint8)
+    _check(k8, "k8", (B, T, H, D), torch.uint8)
+    _check(v8t, "v8t", (load().swa_fp8_v_bytes(B, T, H, D),), torch.uint8)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device=q8.device) if out is None else out
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q8.device) if lse is None else lse
+    if doc_bounds is not None:
+        _check(doc_bounds, "doc_bounds", (B, T, 2), torch.int32)
+    _call("swa_fwd_fp8", _ptr(q8), _ptr(k8), _ptr(v8t), float(q_scale), float(k_scale),
+          float(v_scale), _ptr(doc_bounds), _ptr(o), _ptr(lse), B, T, H, D, int(window),
+          float(scale), _stream())
+    return o, lse
 
 
 def swa_decode_prologue(q, k, v, cos_sin, pos, k_cache, v_cache, eps: float = 1e-6, qn=None):

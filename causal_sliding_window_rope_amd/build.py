@@ -37,9 +37,14 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libswa)")
 
 
+# per-file additions (later flags win): the fp8 packing keeps NaN inputs NaN
+FILE_FLAGS = {"fp8_pack.hip": ["-fhonor-nans"]}
+
+
 def _compile(src: str, extra: list[str]) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [hipcc(), *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o",
+           obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

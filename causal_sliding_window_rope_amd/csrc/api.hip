@@ -342,6 +342,78 @@ int swa_bwd_dq(const void* q, const void* k, const void* v, const void* ve, cons
                                        dtype == SWA_BF16, (hipStream_t)stream), fn);
 }
 
+// ---- fp8 forward variant
+
+static int check_fp8_scale(const char* fn, const char* name, float s) {
+  if (!(std::isfinite(s) && s > 0.f))
+    return fail(SWA_ERR_INVALID_ARG, "%s: %s must be finite and > 0", fn, name);
+  if (!std::isfinite(1.0f / s))
+    return fail(SWA_ERR_INVALID_ARG, "%s: 1/%s is not finite", fn, name);
+  return ok();
+}
+
+int rope_qknorm_fwd_fp8(const void* q, const void* k, const float* cos_sin, void* q8, void* k8,
+                        int B, int T, int H, int D, float eps, swa_dtype dtype, void* stream) {
+  const char* fn = "rope_qknorm_fwd_fp8";
+  SWA_TRY(check_shape(fn, B, T, H, D, dtype));
+  SWA_TRY(need(fn, "q", q)); SWA_TRY(need(fn, "k", k)); SWA_TRY(need(fn, "cos_sin", cos_sin));
+  SWA_TRY(need(fn, "q8", q8)); SWA_TRY(need(fn, "k8", k8));
+  if (!(std::isfinite(eps) && eps >= 0.f))
+    return fail(SWA_ERR_INVALID_ARG, "%s: eps must be finite and >= 0", fn);
+  return hip_status(swa::launch_rope_qknorm_fwd_fp8(q, k, cos_sin, q8, k8, B, T, H, D, eps,
+                                                    dtype == SWA_BF16, (hipStream_t)stream), fn);
+}
+
+size_t swa_fp8_v_bytes(int B, int T, int H, int D) {
+  if (B < 1 || T < 1 || H < 1 || (D != 64 && D != 128)) return 0;
+  return swa::fp8_v_bytes(B, T, H, D);
+}
+
+int swa_fp8_pack(const void* q, const void* k, const void* v, float q_scale, float k_scale,
+                 float v_scale, void* q8, void* k8, void* v8t, int B, int T, int H, int D,
+                 swa_dtype dtype, void* stream) {
+  const char* fn = "swa_fp8_pack";
+  SWA_TRY(check_shape(fn, B, T, H, D, dtype));
+  if ((q == nullptr) != (q8 == nullptr) || (k == nullptr) != (k8 == nullptr) ||
+      (v == nullptr) != (v8t == nullptr))
+    return fail(SWA_ERR_INVALID_ARG, "%s: each of (q, q8), (k, k8), (v, v8t) must be both set "
+                "or both NULL", fn);
+  if (!q && !k && !v) return fail(SWA_ERR_INVALID_ARG, "%s: nothing to pack", fn);
+  if (q) {
+    SWA_TRY(need(fn, "q", q)); SWA_TRY(need(fn, "q8", q8));
+    SWA_TRY(check_fp8_scale(fn, "q_scale", q_scale));
+  }
+  if (k) {
+    SWA_TRY(need(fn, "k", k)); SWA_TRY(need(fn, "k8", k8));
+    SWA_TRY(check_fp8_scale(fn, "k_scale", k_scale));
+  }
+  if (v) {
+    SWA_TRY(need(fn, "v", v)); SWA_TRY(need(fn, "v8t", v8t));
+    SWA_TRY(check_fp8_scale(fn, "v_scale", v_scale));
+  }
+  return hip_status(swa::launch_fp8_pack(q, k, v, 1.0f / q_scale, 1.0f / k_scale, 1.0f / v_scale,
+                                         q8, k8, v8t, B, T, H, D, dtype == SWA_BF16,
+                                         (hipStream_t)stream), fn);
+}
+
+int swa_fwd_fp8(const void* q8, const void* k8, const void* v8t, float q_scale, float k_scale,
+                float v_scale, const int* doc_bounds, void* o, float* lse, int B, int T, int H,
+                int D, int window, float scale, void* stream) {
+  const char* fn = "swa_fwd_fp8";
+  SWA_TRY(check_shape(fn, B, T, H, D, SWA_BF16));
+  SWA_TRY(need(fn, "q8", q8)); SWA_TRY(need(fn, "k8", k8)); SWA_TRY(need(fn, "v8t", v8t));
+  SWA_TRY(need(fn, "o", o)); SWA_TRY(need(fn, "lse", lse));
+  SWA_TRY(opt(fn, "doc_bounds", doc_bounds));
+  SWA_TRY(check_fp8_scale(fn, "q_scale", q_scale));
+  SWA_TRY(check_fp8_scale(fn, "k_scale", k_scale));
+  SWA_TRY(check_fp8_scale(fn, "v_scale", v_scale));
+  swa::AttnShape a{B, T, H, D, 0, scale};
+  a.bounds = doc_bounds;
+  SWA_TRY(check_window_scale(fn, window, scale, T, &a.window));
+  return hip_status(swa::launch_fwd_fp8(a, q8, k8, v8t, q_scale * k_scale, v_scale, o, lse,
+                                        (hipStream_t)stream), fn);
+}
+
 // ---- sliding-window decoding from a ring K/V cache
 
 static int check_decode_shape(const char* fn, int B, int H, int D, int cap, int dtype) {

@@ -144,6 +144,28 @@ __device__ __forceinline__ const E* ve_row(const E* ve, const int* ids, int rows
   return ve + (((size_t)b * T + t) * H + h) * D;
 }
 
+// Keys visible to this lane's query row: [lo, lo + n) (causal window, sequence end and, with
+// document masking, the start of the row's document); wlo0 / wlo1: lo of the wave's first and
+// last query (lo never decreases along a row, so these bound the whole wave).
+struct RowRange {
+  int lo;
+  unsigned n;
+  int wlo0, wlo1;
+};
+
+template <bool DOC>
+__device__ __forceinline__ RowRange row_range(const int* bounds, int b, int T, int W, int myq) {
+  const int qc = min(myq, T - 1);
+  int start = 0;
+  if constexpr (DOC) start = bounds[2 * ((size_t)b * T + qc)];
+  RowRange r;
+  r.lo = max(qc - W + 1, start);
+  r.n = (unsigned)(qc - r.lo + 1);
+  r.wlo0 = __builtin_amdgcn_readlane(r.lo, 0);
+  r.wlo1 = __builtin_amdgcn_readlane(r.lo, 31);
+  return r;
+}
+
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

@@ -127,28 +127,6 @@ struct WaveState {
   float m_ref, l_run;
 };
 
-// Keys visible to this lane's query row: [lo, lo + n) (causal window, sequence end and, with
-// document masking, the start of the row's document); wlo0 / wlo1: lo of the wave's first and
-// last query (lo never decreases along a row, so these bound the whole wave).
-struct RowRange {
-  int lo;
-  unsigned n;
-  int wlo0, wlo1;
-};
-
-template <bool DOC>
-__device__ __forceinline__ RowRange row_range(const int* bounds, int b, int T, int W, int myq) {
-  const int qc = min(myq, T - 1);
-  int start = 0;
-  if constexpr (DOC) start = bounds[2 * ((size_t)b * T + qc)];
-  RowRange r;
-  r.lo = max(qc - W + 1, start);
-  r.n = (unsigned)(qc - r.lo + 1);
-  r.wlo0 = __builtin_amdgcn_readlane(r.lo, 0);
-  r.wlo1 = __builtin_amdgcn_readlane(r.lo, 31);
-  return r;
-}
-
 // One 64-key tile for one wave (32 query rows): S^T = K Q^T, mask, online softmax, O^T += V^T P^T.
 template <int D>
 __device__ __forceinline__ void tile_step(WaveState<D>& ws, const bf16x8* qreg,

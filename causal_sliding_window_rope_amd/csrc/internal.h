@@ -32,6 +32,15 @@ hipError_t launch_ve_gate(const void* x, int ldx, const float* Wg, float* gate, 
 hipError_t launch_ve_gate_dv(const void* dv, const void* ve, const int* ids, int ve_rows,
                              const float* gate, void* dve, float* dgate, int B, int T, int H,
                              int D, bool bf16, hipStream_t s);
+hipError_t launch_rope_qknorm_fwd_fp8(const void* q, const void* k, const float* cs, void* q8,
+                                      void* k8, int B, int T, int H, int D, float eps, bool bf16,
+                                      hipStream_t s);
+size_t fp8_v_bytes(int B, int T, int H, int D);
+hipError_t launch_fp8_pack(const void* q, const void* k, const void* v, float q_inv, float k_inv,
+                           float v_inv, void* q8, void* k8, void* v8t, int B, int T, int H,
+                           int D, bool bf16, hipStream_t s);
+hipError_t launch_fwd_fp8(const AttnShape& a, const void* q8, const void* k8, const void* v8t,
+                          float qk_scale, float v_scale, void* o, float* lse, hipStream_t s);
 size_t gate_bwd_workspace_bytes(int B, int T, int H);
 hipError_t launch_ve_gate_bwd(const void* x, int ldx, const float* Wg, const float* gate,
                               const float* dgate, float* dWg, void* dx32, void* ws, int B, int T,

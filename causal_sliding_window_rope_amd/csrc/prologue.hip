@@ -92,10 +92,13 @@ __device__ __forceinline__ void rotate(float* y, const float* x, const float* ot
   }
 }
 
-template <typename E, int D>
+// OUT8: the normalised rows are written as e4m3 codes (scale 1; every entry of a normalised
+// row is below sqrt(D) <= 11.4 in magnitude, far inside e4m3's range, so no saturation) for
+// the fp8 forward; qn / kn then point to bytes.
+template <typename E, int D, bool OUT8>
 __global__ void __launch_bounds__(256) rope_qknorm_fwd_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const float* __restrict__ cs,
-    E* __restrict__ qn, E* __restrict__ kn, int rows_per_tensor, int T, int H, float eps) {
+    void* __restrict__ qn, void* __restrict__ kn, int rows_per_tensor, int T, int H, float eps) {
   using W = RowWord<E>;
   constexpr int VPT = W::VPT, TPR = D / VPT, HALF_T = TPR / 2;
   const int lane_in_row = threadIdx.x % TPR;
@@ -121,7 +124,20 @@ __global__ void __launch_bounds__(256) rope_qknorm_fwd_kernel(
   W out;
 #pragma unroll
   for (int e = 0; e < VPT; ++e) out.v[e] = y[e] * rinv;
-  out.store((is_k ? kn : qn) + off);
+  if constexpr (OUT8) {
+    unsigned w[VPT / 4];
+#pragma unroll
+    for (int j = 0; j < VPT / 4; ++j) {
+      const unsigned lo =
+          __builtin_amdgcn_cvt_pk_fp8_f32(out.v[4 * j], out.v[4 * j + 1], 0u, false);
+      w[j] = __builtin_amdgcn_cvt_pk_fp8_f32(out.v[4 * j + 2], out.v[4 * j + 3], lo, true);
+    }
+    unsigned char* dst = static_cast<unsigned char*>(is_k ? kn : qn) + off;
+    if constexpr (VPT == 8) *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+    else *reinterpret_cast<unsigned*>(dst) = w[0];
+  } else {
+    out.store(static_cast<E*>(is_k ? kn : qn) + off);
+  }
 }
 
 template <typename E, int D>
@@ -167,16 +183,27 @@ __global__ void __launch_bounds__(256) rope_qknorm_bwd_kernel(
   out.store((is_k ? dk : dq) + off);
 }
 
-template <typename E, int D>
+template <typename E, int D, bool OUT8 = false>
 static hipError_t launch_fwd_t(const void* q, const void* k, const float* cs, void* qn, void* kn,
                                int B, int T, int H, float eps, hipStream_t s) {
   constexpr int TPR = D / (16 / sizeof(E));
   const int rows = B * T * H;
   const int rpb = 256 / TPR;
   const int blocks = (2 * rows + rpb - 1) / rpb;
-  hipLaunchKernelGGL((rope_qknorm_fwd_kernel<E, D>), dim3(blocks), dim3(256), 0, s,
-                     (const E*)q, (const E*)k, cs, (E*)qn, (E*)kn, rows, T, H, eps);
+  hipLaunchKernelGGL((rope_qknorm_fwd_kernel<E, D, OUT8>), dim3(blocks), dim3(256), 0, s,
+                     (const E*)q, (const E*)k, cs, qn, kn, rows, T, H, eps);
   return hipGetLastError();
+}
+
+hipError_t launch_rope_qknorm_fwd_fp8(const void* q, const void* k, const float* cs, void* q8,
+                                      void* k8, int B, int T, int H, int D, float eps, bool bf16,
+                                      hipStream_t s) {
+  if (bf16) {
+    return D == 64 ? launch_fwd_t<swa::bf16, 64, true>(q, k, cs, q8, k8, B, T, H, eps, s)
+                   : launch_fwd_t<swa::bf16, 128, true>(q, k, cs, q8, k8, B, T, H, eps, s);
+  }
+  return D == 64 ? launch_fwd_t<float, 64, true>(q, k, cs, q8, k8, B, T, H, eps, s)
+                 : launch_fwd_t<float, 128, true>(q, k, cs, q8, k8, B, T, H, eps, s);
 }
 
 template <typename E, int D>

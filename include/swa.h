@@ -251,6 +251,58 @@ int swa_bwd_dq(const void* q, const void* k, const void* v, const void* ve, cons
  */
 
 /*
+ * fp8 forward variant ("从4万美元到73美元", intelliparadigm.com, the paragraph on mixed
+ * precision: fp8 doubles matrix throughput over bf16 and needs scales to stay accurate).
+ * Format: OCP e4m3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, no
+ * infinities, largest finite 448, S.1111.111 = NaN), the format gfx950's fp8 MFMA reads.
+ * Calibration: one float32 scale per tensor, x ~= scale * e4m3 value.
+ *
+ * swa_fp8_v_bytes — bytes of the packed V operand: B*H*D*Tp with Tp = T rounded up to 64.
+ */
+size_t swa_fp8_v_bytes(int B, int T, int H, int D);
+
+/*
+ * swa_fp8_pack — quantise q, k, v (dtype, (B,T,H,D), normally q_hat, k_hat from
+ *   rope_qknorm_fwd and v or v_eff) to e4m3 codes of x / scale: a float32 multiply by the
+ *   float32 reciprocal of the scale, then round to nearest even, saturating finite values
+ *   beyond 448 (and infinities) to +-448; NaN stays NaN. Each pair (q, q8), (k, k8), (v, v8t)
+ *   is either both set or both NULL (at least one set).
+ *   q8, k8: device (B,T,H,D) bytes, written.   v8t: device, swa_fp8_v_bytes() bytes, written:
+ *   per (b, h) a D x Tp byte matrix (row d = dimension d, V transposed), in which every block
+ *   of 64 keys starting at 64t stores key 64t + 32kb + 8a + 4g + c at column
+ *   64t + 32g + 16kb + 4a + c (kb, g in {0,1}; a, c in 0..3): the order in which the forward
+ *   kernel's probabilities leave its score accumulators. Keys >= T are 0.
+ *   Scales: finite, > 0, with a finite reciprocal. q_hat and k_hat need no calibration: their
+ *   entries are bounded by sqrt(D) < 448, so scale 1 keeps them in range.
+ */
+int swa_fp8_pack(const void* q, const void* k, const void* v, float q_scale, float k_scale,
+                 float v_scale, void* q8, void* k8, void* v8t, int B, int T, int H, int D,
+                 swa_dtype dtype, void* stream);
+
+/*
+ * rope_qknorm_fwd_fp8 — rope_qknorm_fwd writing q_hat, k_hat directly as e4m3 codes at scale 1
+ *   (float32 results rounded once to nearest even; every entry of a normalised row is below
+ *   sqrt(D) in magnitude, so no saturation occurs). Feeds swa_fwd_fp8 (q_scale = k_scale = 1)
+ *   without a separate quantisation pass. Arguments as rope_qknorm_fwd; q8, k8: device
+ *   (B,T,H,D) bytes, written.
+ */
+int rope_qknorm_fwd_fp8(const void* q, const void* k, const float* cos_sin, void* q8, void* k8,
+                        int B, int T, int H, int D, float eps, swa_dtype dtype, void* stream);
+
+/*
+ * swa_fwd_fp8 — swa_fwd on fp8 operands: s_ij = scale * q_scale * k_scale * (q8_i . k8_j) on
+ *   the e4m3 values (exact products, float32 accumulation), online softmax in float32,
+ *   probabilities rounded to e4m3 as the PV operand (the running reference keeps them <= 2^8),
+ *   O = v_scale * sum_j P_ij v8_j / l_i in float32, stored as bf16. lse from the float32 sums.
+ *   q8, k8, v8t, scales: as written by swa_fp8_pack.   doc_bounds: as for swa_fwd.
+ *   o: device (B,T,H,D) bf16, written.   lse: device (B,H,T) float, natural log, written.
+ *   Forward only: the backward of this variant is not provided.
+ */
+int swa_fwd_fp8(const void* q8, const void* k8, const void* v8t, float q_scale, float k_scale,
+                float v_scale, const int* doc_bounds, void* o, float* lse, int B, int T, int H,
+                int D, int window, float scale, void* stream);
+
+/*
  * swa_decode_prologue — RoPE at angle pos[b] * theta_i and the RMS QK-norm of the new q and k
  *   (as rope_qknorm_fwd at row pos[b]); writes qn and stores the normalised k and the raw v in
  *   slot pos[b] mod cap of the caches.

@@ -156,6 +156,29 @@ def test_swa_bwd_validation(lib):
     assert dq(ve=P, gate=P, ids=P, rows=0) == INVALID   # table mode without rows
 
 
+def test_fp8_validation(lib):
+    assert lib.swa_fp8_v_bytes(2, 100, 3, 128) == 2 * 3 * 128 * 128     # T padded to 128
+    assert lib.swa_fp8_v_bytes(2, 100, 3, 96) == 0
+
+    def pack(q=P, k=P, v=P, q8=P, k8=P, v8=P, sq=1.0, sk=1.0, sv=1.0, D=64):
+        return lib.swa_fp8_pack(q, k, v, sq, sk, sv, q8, k8, v8, 1, 8, 2, D, 1, None)
+
+    assert pack(q8=None) == INVALID                      # q without q8
+    assert pack(q=None, k=None, v=None, q8=None, k8=None, v8=None) == INVALID   # nothing to do
+    assert pack(sv=0.0) == INVALID and pack(sq=float("nan")) == INVALID
+    assert pack(sk=1e-39) == INVALID                     # reciprocal overflows
+    assert pack(v8=MIS) == ALIGN
+    assert pack(D=96) == UNSUPPORTED
+
+    def fwd(q8=P, k8=P, v8=P, sq=1.0, W=4, scale=0.125, doc=None):
+        return lib.swa_fwd_fp8(q8, k8, v8, sq, 1.0, 1.0, doc, P, P, 1, 8, 2, 64, W, scale, None)
+
+    assert fwd(q8=None) == INVALID
+    assert fwd(sq=-1.0) == INVALID
+    assert fwd(W=0) == INVALID and fwd(scale=0.0) == INVALID
+    assert fwd(doc=MIS) == ALIGN
+
+
 def test_prologue_and_gate_validation(lib):
     assert lib.rope_table(None, 8, 64, 1e4, None) == INVALID
     assert lib.rope_table(P, 8, 48, 1e4, None) == UNSUPPORTED

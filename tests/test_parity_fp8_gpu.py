@@ -1,0 +1,167 @@
+"""GPU parity of the fp8 forward variant against the oracle, through the C ABI.
+
+* swa_fp8_pack: the e4m3 codes of q, k (natural layout) and of v (the packed, transposed,
+  key-permuted layout documented in swa.h, undone here from that description) equal the
+  oracle quantiser's codes bit for bit, bf16 and float32 inputs, ragged T (keys past T are 0).
+* rope_qknorm_fwd_fp8: codes of the normalised rows equal the oracle's (float64 prologue,
+  then e4m3 rounding) except where the value lies within float32 rounding distance of an e4m3
+  rounding boundary: there the kernel's float32 value decides, and either neighbour is valid.
+* swa_fwd_fp8 on those codes against the plain attention of the decoded inputs
+  (oracle.fp8.attention_fwd_fp8). Bar: the kernel rounds each probability to e4m3 for the PV
+  product (3 mantissa bits: relative rounding error at most 2^-4, about 2^-4/sqrt(3) on
+  average), so O is held to relative L2 <= 2^-4 and lse (float32 sums of the unrounded
+  probabilities) to the bf16 path's 2e-3. With one visible key the probability is exactly 1
+  and O is the decoded value row up to the bf16 store (relative 2^-9).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from causal_sliding_window_rope_amd import binding as sw
+from causal_sliding_window_rope_amd.inputs import make_inputs, small_workload
+import oracle
+from oracle import fp8
+from gpu_helpers import BF16_LSE_ABS, announce, dev, host, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+FP8_REL_L2 = 2.0 ** -4
+
+
+def unpack_v8t(v8t: np.ndarray, B: int, T: int, H: int, D: int) -> np.ndarray:
+    """(B, T, H, D) codes from the packed layout, as swa.h describes it."""
+    Tp = (T + 63) // 64 * 64
+    m = v8t.reshape(B, H, D, Tp)
+    out = np.zeros((B, Tp, H, D), dtype=np.uint8)
+    for kb in range(2):
+        for a in range(4):
+            for g in range(2):
+                for c in range(4):
+                    key = 32 * kb + 8 * a + 4 * g + c
+                    col = 32 * g + 16 * kb + 4 * a + c
+                    out[:, key::64] = m[:, :, :, col::64].transpose(0, 3, 1, 2)
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_pack_codes_bit_exact(dtype, D):
+    B, T, H = 2, 200, 3
+    announce("fp8 pack", dtype, D)
+    wl = small_workload(B, T, H, D, T, dtype, seed=D)
+    x = make_inputs(wl)
+    sq, sk, sv = 0.05, 1.0, 1.0 / 64
+    q8, k8, v8t = sw.swa_fp8_pack(dev(x["q"], dtype), dev(x["k"], dtype), dev(x["v"], dtype),
+                                  sq, sk, sv)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(q8.cpu().numpy(), fp8.quantize(x["q"], sq))
+    np.testing.assert_array_equal(k8.cpu().numpy(), fp8.quantize(x["k"], sk))
+    got_v = unpack_v8t(v8t.cpu().numpy(), B, T, H, D)
+    np.testing.assert_array_equal(got_v[:, :T], fp8.quantize(x["v"], sv))
+    assert np.all(got_v[:, T:] == 0)
+
+
+def test_pack_saturates_and_keeps_nan():
+    B, T, H, D = 1, 64, 1, 64
+    announce("fp8 pack saturation")
+    v = np.zeros((B, T, H, D), dtype=np.float32)
+    v[0, 0, 0, :6] = [500.0, -1e6, 448.0, 447.0, np.nan, 2.0 ** -11]
+    q8, _, _ = sw.swa_fp8_pack(q=torch.from_numpy(v).cuda())
+    torch.cuda.synchronize()
+    codes = q8.cpu().numpy()[0, 0, 0, :6]
+    assert codes[:4].tolist() == [0x7E, 0xFE, 0x7E, 0x7E]
+    assert codes[4] & 0x7F == 0x7F and codes[5] == 0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_prologue_fp8_codes(dtype, D):
+    B, T, H = 2, 150, 3
+    announce("fp8 prologue", dtype, D)
+    x = make_inputs(small_workload(B, T, H, D, T, dtype, seed=5 + D))
+    cs = sw.rope_table(T, D, 10000.0)
+    q8, k8 = sw.rope_qknorm_fwd_fp8(dev(x["q"], dtype), dev(x["k"], dtype), cs)
+    torch.cuda.synchronize()
+    for got, name in ((q8, "q"), (k8, "k")):
+        xh, _ = oracle.rope_qknorm(x[name].astype(np.float64), 10000.0, 1e-6)
+        got = got.cpu().numpy()
+        want = fp8.e4m3_encode(xh)
+        lo, hi = fp8.e4m3_encode(xh * (1 - 1e-5)), fp8.e4m3_encode(xh * (1 + 1e-5))
+        assert np.all((got == want) | (got == lo) | (got == hi)), name
+        assert np.mean(got == want) > 0.999, name
+    # the codes drive the fp8 forward like packed ones
+    o, _ = sw.swa_fwd_fp8(q8, k8, sw.swa_fp8_pack(v=dev(x["v"], dtype), v_scale=1 / 64)[2], T,
+                          v_scale=1 / 64)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+
+
+CASES = [  # B, T, H, D, W, q_scale, v_scale
+    (2, 300, 2, 128, 100, 1.0, 1.0 / 64),
+    (2, 257, 3, 128, 257, 0.05, 1.0 / 32),     # full causal, ragged tail
+    (1, 640, 2, 128, 1024, 1.0, 1.0 / 64),     # window beyond T
+    (2, 200, 2, 64, 64, 1.0, 1.0 / 64),
+    (1, 130, 2, 64, 130, 0.1, 1.0),
+]
+
+
+def _run(x, B, T, H, D, W, sq, sv, doc=None):
+    q8, k8, v8t = sw.swa_fp8_pack(dev(x["q"], "bf16"), dev(x["k"], "bf16"), dev(x["v"], "bf16"),
+                                  sq, 1.0, sv)
+    bounds = None
+    if doc is not None:
+        bounds = sw.swa_doc_bounds(torch.from_numpy(doc.astype(np.int32)).cuda())
+    o, lse = sw.swa_fwd_fp8(q8, k8, v8t, W, sq, 1.0, sv, doc_bounds=bounds)
+    torch.cuda.synchronize()
+    want_o, want_lse = fp8.attention_fwd_fp8(fp8.quantize(x["q"], sq), fp8.quantize(x["k"], 1.0),
+                                             fp8.quantize(x["v"], sv), sq, 1.0, sv, W,
+                                             1.0 / np.sqrt(D), doc_id=doc)
+    return host(o), host(lse), want_o, want_lse
+
+
+@pytest.mark.parametrize("B,T,H,D,W,sq,sv", CASES)
+def test_fwd_fp8_against_oracle(B, T, H, D, W, sq, sv):
+    announce("fp8 fwd", B, T, H, D, W, sq, sv)
+    wl = small_workload(B, T, H, D, W, "bf16", seed=T + D)
+    x = make_inputs(wl)
+    o, lse, want_o, want_lse = _run(x, B, T, H, D, W, sq, sv)
+    assert np.all(np.isfinite(o))
+    err = rel_l2(o, want_o)
+    assert err <= FP8_REL_L2, f"O rel L2 {err:.4g}"
+    assert np.max(np.abs(lse - want_lse)) <= BF16_LSE_ABS
+
+
+def test_fwd_fp8_single_key_is_the_value_row():
+    B, T, H, D = 2, 150, 2, 128
+    announce("fp8 fwd window 1")
+    x = make_inputs(small_workload(B, T, H, D, 1, "bf16", seed=9))
+    o, lse, want_o, want_lse = _run(x, B, T, H, D, 1, 1.0, 1.0 / 64)
+    assert rel_l2(o, want_o) <= 2.0 ** -9
+    assert np.max(np.abs(lse - want_lse)) <= 1e-4
+
+
+def test_fwd_fp8_document_mask():
+    B, T, H, D, W = 2, 384, 2, 128, 200
+    announce("fp8 fwd documents")
+    x = make_inputs(small_workload(B, T, H, D, W, "bf16", seed=21, doc_mean=60))
+    o, lse, want_o, want_lse = _run(x, B, T, H, D, W, 1.0, 1.0 / 64, doc=x["doc_id"])
+    assert rel_l2(o, want_o) <= FP8_REL_L2
+    assert np.max(np.abs(lse - want_lse)) <= BF16_LSE_ABS
+
+
+def test_fwd_fp8_close_to_bf16_kernel():
+    """On the same values the fp8 and bf16 kernels compute the same attention. Besides the
+    probability rounding, the fp8 path rounds q and k to e4m3, which moves each score by about
+    0.05 (standard deviation) at these magnitudes, so the bars here are looser: O relative L2
+    within 0.1 and lse within 0.3."""
+    B, T, H, D, W = 2, 512, 2, 128, 256
+    announce("fp8 vs bf16 kernel")
+    x = make_inputs(small_workload(B, T, H, D, W, "bf16", seed=33))
+    q, k, v = (dev(x[n], "bf16") for n in ("q", "k", "v"))
+    o16, l16 = sw.swa_fwd(q, k, v, W)
+    q8, k8, v8t = sw.swa_fp8_pack(q, k, v, 1.0, 1.0, 1.0 / 64)
+    o8, l8 = sw.swa_fwd_fp8(q8, k8, v8t, W, 1.0, 1.0, 1.0 / 64)
+    torch.cuda.synchronize()
+    assert rel_l2(host(o8), host(o16)) <= 0.1
+    assert float((l8 - l16).abs().max()) <= 0.3
