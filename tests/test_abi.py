@@ -177,6 +177,10 @@ def test_fp8_validation(lib):
     assert fwd(sq=-1.0) == INVALID
     assert fwd(W=0) == INVALID and fwd(scale=0.0) == INVALID
     assert fwd(doc=MIS) == ALIGN
+    assert lib.rope_qknorm_fwd_fp8(P, P, P, None, P, 1, 8, 2, 64, 1e-6, 1, None) == INVALID
+    assert lib.rope_qknorm_fwd_fp8(P, P, P, P, MIS, 1, 8, 2, 64, 1e-6, 1, None) == ALIGN
+    assert lib.rope_qknorm_fwd_fp8(P, P, P, P, P, 1, 8, 2, 64, -1.0, 1, None) == INVALID
+    assert lib.rope_qknorm_fwd_fp8(P, P, P, P, P, 1, 8, 2, 32, 1e-6, 1, None) == UNSUPPORTED
 
 
 def test_prologue_and_gate_validation(lib):
