@@ -3,7 +3,7 @@
 
 One step = the attention of every layer of the nanochat d24 model, forward then backward,
 as in a training step: for layers 0..23 rope_qknorm_fwd + swa_fwd, then for layers 23..0
-swa_bwd (preprocess, dK/dV, dQ) + rope_qknorm_bwd. Windows follow the 3-short:1-long
+swa_bwd (dQ with the row terms, then dK/dV) + rope_qknorm_bwd. Windows follow the 3-short:1-long
 tiling (layers 3, 7, ... full 2048, the rest 1024); B=16 sequences of T=2048, H=12, D=128,
 bf16 storage, fp32 accumulation. Inputs are synthetic N(0, 1) tensors drawn on the device
 from a seeded generator, one set per layer (kernel time does not depend on the values).
@@ -191,20 +191,17 @@ def run_bench(args):
                 fids, frows = ids, rows
             elif cfg["gate"]:
                 v = t["veff"]
+            # dQ first: its kernel also writes the row terms (delta, lse) that dK/dV reads
             if rec: rec["bwd"][li][0].record()
-            call("swa_bwd_preprocess", P(t["o"]), P(t["dO"]), P(t["lse"]), P(ws), nws, B, T, H, D,
-                 sw.SWA_BF16, stream)
+            call("swa_bwd_dq_rowterms", P(t["qn"]), P(t["kn"]), P(v), P(ve), P(gate), P(fids),
+                 frows, P(bounds), P(t["o"]), P(t["lse"]), P(t["dO"]), P(g["dqn"]), P(ws), nws,
+                 B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
             if rec: rec["bwd"][li][1].record()
             call("swa_bwd_dkdv", P(t["qn"]), P(t["kn"]), P(v), P(ve), P(gate), P(fids), frows,
                  P(bounds), P(t["lse"]),
                  P(t["dO"]), P(g["dkn"]), P(g["dv"]), P(dve), P(dgate), P(ws), nws,
                  B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
             if rec: rec["bwd"][li][2].record()
-            call("swa_bwd_dq", P(t["qn"]), P(t["kn"]), P(v), P(ve), P(gate), P(fids), frows,
-                 P(bounds), P(t["lse"]),
-                 P(t["dO"]), P(g["dqn"]), P(ws), nws, B, T, H, D, t["W"], scale, sw.SWA_BF16,
-                 stream)
-            if rec: rec["bwd"][li][3].record()
             call("rope_qknorm_bwd", P(t["q"]), P(t["k"]), P(cs), P(g["dqn"]), P(g["dkn"]), P(g["dq"]),
                  P(g["dk"]), B, T, H, D, 1e-6, sw.SWA_BF16, stream)
             if cfg["gate"]:
@@ -219,7 +216,7 @@ def run_bench(args):
         step(None)
     torch.cuda.synchronize()
     nl = len(layers)
-    recs = [{"fwd": [[ev(), ev()] for _ in range(nl)], "bwd": [[ev() for _ in range(4)] for _ in range(nl)]}
+    recs = [{"fwd": [[ev(), ev()] for _ in range(nl)], "bwd": [[ev() for _ in range(3)] for _ in range(nl)]}
             for _ in range(args.steps)]
     e0, e1 = ev(), ev()
     torch.cuda.synchronize()          # one GPU: no process group, so no barrier is needed
@@ -233,9 +230,8 @@ def run_bench(args):
     step_ms = e0.elapsed_time(e1) / args.steps
 
     fwd_ms = sum(r["fwd"][l][0].elapsed_time(r["fwd"][l][1]) for r in recs for l in range(nl))
-    pre_ms = sum(r["bwd"][l][0].elapsed_time(r["bwd"][l][1]) for r in recs for l in range(nl))
+    dq_ms = sum(r["bwd"][l][0].elapsed_time(r["bwd"][l][1]) for r in recs for l in range(nl))
     kv_ms = sum(r["bwd"][l][1].elapsed_time(r["bwd"][l][2]) for r in recs for l in range(nl))
-    dq_ms = sum(r["bwd"][l][2].elapsed_time(r["bwd"][l][3]) for r in recs for l in range(nl))
     launches = args.steps * nl
 
     npairs = sum(visible_pairs(cfg, W, starts) for W in cfg["windows"]) * H
@@ -243,7 +239,7 @@ def run_bench(args):
     bwd_flop = 10 * D * npairs
     flop = fwd_flop + bwd_flop
     value = flop / (step_ms * 1e-3) / 1e12
-    core_ms = (fwd_ms + pre_ms + kv_ms + dq_ms) / args.steps
+    core_ms = (fwd_ms + kv_ms + dq_ms) / args.steps
     fwd_tf = fwd_flop / (fwd_ms / args.steps * 1e-3) / 1e12
     bwd_tf = bwd_flop / ((kv_ms + dq_ms) / args.steps * 1e-3) / 1e12
     # algorithmic FLOPs of each backward kernel: dK/dV kernel recomputes S and dP and forms dV,
@@ -255,7 +251,7 @@ def run_bench(args):
     # dominant kernel: the one with the largest share of the step
     cands = [("dkdv_bf16_kernel (swa_bwd_dkdv)", kv_ms, kv_flop),
              ("fwd_bf16_kernel (swa_fwd)", fwd_ms, fwd_flop),
-             ("dq_bf16_kernel (swa_bwd_dq)", dq_ms, dq_flop)]
+             ("dq_bf16_kernel (swa_bwd_dq_rowterms)", dq_ms, dq_flop)]
     dom, dom_total_ms, dom_total_flop = max(cands, key=lambda x: x[1])
     dom_ms, dom_flop = dom_total_ms / launches, dom_total_flop / nl
     achieved = dom_flop / (dom_ms * 1e-3) / 1e12
@@ -286,7 +282,6 @@ def run_bench(args):
             "swa_bwd_dkdv_tflops_executed": round(kv_flop / (kv_ms / args.steps * 1e-3) / 1e12, 2),
             "swa_bwd_dq_tflops_executed": round(dq_flop / (dq_ms / args.steps * 1e-3) / 1e12, 2),
             "swa_fwd_ms_per_step": round(fwd_ms / args.steps, 4),
-            "swa_bwd_preprocess_ms_per_step": round(pre_ms / args.steps, 4),
             "swa_bwd_dkdv_ms_per_step": round(kv_ms / args.steps, 4),
             "swa_bwd_dq_ms_per_step": round(dq_ms / args.steps, 4),
             "wall_s_timed_region": round(wall, 3),

@@ -44,6 +44,8 @@ SIGNATURES = {
                           _I, _I, _I, _I, _I, _F, _I, _P]),
     "swa_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I,
                         _F, _I, _P]),
+    "swa_bwd_dq_rowterms": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _S, _I, _I,
+                                 _I, _I, _I, _F, _I, _P]),
     "swa_fp8_v_bytes": (_S, [_I, _I, _I, _I]),
     "rope_qknorm_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "swa_fp8_pack": (_I, [_P, _P, _P, _F, _F, _F, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
@@ -295,8 +297,10 @@ def swa_bwd(q, k, v, o, lse, dO, window: int, scale: float | None = None, ve=Non
 
 
 def swa_bwd_stages(q, k, v, o, lse, dO, window: int, scale: float | None = None, ve=None,
-                   gate=None, workspace=None, grads=None, doc_bounds=None, ve_ids=None):
-    """swa_bwd as its three C-ABI stages: preprocess, dK/dV, dQ."""
+                   gate=None, workspace=None, grads=None, doc_bounds=None, ve_ids=None,
+                   preprocess: bool = False):
+    """swa_bwd as its C-ABI stages: dQ with the row terms, then dK/dV (the one-call order), or
+    with preprocess=True: preprocess, dK/dV, dQ."""
     B, T, H, D = q.shape
     ids, rows = _ve_table(ve, gate, ve_ids, B, T, H, D, q.dtype)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
@@ -307,17 +311,18 @@ def swa_bwd_stages(q, k, v, o, lse, dO, window: int, scale: float | None = None,
     dq, dk, dv, dve, dgate = _grads(q, ve, ve_ids, B, T, H) if grads is None else grads
     st = _stream()
     dt = _dt(q)
-    _call("swa_bwd_preprocess", _ptr(o), _ptr(dO), _ptr(lse), _ptr(workspace), nbytes, B, T, H, D, dt,
-          st)
-    _call("swa_bwd_dkdv", _ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), ids, rows,
-          _ptr(doc_bounds),
-          _ptr(lse), _ptr(dO),
-          _ptr(dk), _ptr(dv), _ptr(dve), _ptr(dgate), _ptr(workspace), nbytes, B, T, H, D,
-          int(window), float(scale), dt, st)
-    _call("swa_bwd_dq", _ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), ids, rows,
-          _ptr(doc_bounds),
-          _ptr(lse), _ptr(dO),
-          _ptr(dq), _ptr(workspace), nbytes, B, T, H, D, int(window), float(scale), dt, st)
+    common = (_ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), ids, rows, _ptr(doc_bounds))
+    if preprocess:
+        _call("swa_bwd_preprocess", _ptr(o), _ptr(dO), _ptr(lse), _ptr(workspace), nbytes, B, T, H,
+              D, dt, st)
+    else:
+        _call("swa_bwd_dq_rowterms", *common, _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq),
+              _ptr(workspace), nbytes, B, T, H, D, int(window), float(scale), dt, st)
+    _call("swa_bwd_dkdv", *common, _ptr(lse), _ptr(dO), _ptr(dk), _ptr(dv), _ptr(dve), _ptr(dgate),
+          _ptr(workspace), nbytes, B, T, H, D, int(window), float(scale), dt, st)
+    if preprocess:
+        _call("swa_bwd_dq", *common, _ptr(lse), _ptr(dO), _ptr(dq), _ptr(workspace), nbytes, B, T,
+              H, D, int(window), float(scale), dt, st)
     if ve is not None:
         return dq, dk, dv, dve, dgate
     return dq, dk, dv

@@ -291,10 +291,10 @@ int swa_bwd(const void* q, const void* k, const void* v, const void* ve, const f
                     dgate, workspace, ws_bytes, B, T, H, D, window, scale, dtype, &a));
   const bool bf = dtype == SWA_BF16;
   const hipStream_t s = (hipStream_t)stream;
-  hipError_t e = swa::launch_bwd_pre(a, o, dO, lse, workspace, bf, s);
+  // dQ first: it also writes the row terms that the key-major dK/dV kernel reads
+  hipError_t e = swa::launch_bwd_dq_rowterms(a, q, k, v, ve, gate, o, lse, dO, dq, workspace, bf, s);
   if (e == hipSuccess)
     e = swa::launch_bwd_dkdv(a, q, k, v, ve, gate, lse, dO, dk, dv, dve, dgate, workspace, bf, s);
-  if (e == hipSuccess) e = swa::launch_bwd_dq(a, q, k, v, ve, gate, lse, dO, dq, workspace, bf, s);
   return hip_status(e, fn);
 }
 
@@ -340,6 +340,23 @@ int swa_bwd_dq(const void* q, const void* k, const void* v, const void* ve, cons
   SWA_TRY(check_ws(fn, workspace, ws_bytes, B, T, H, D, dtype));
   return hip_status(swa::launch_bwd_dq(a, q, k, v, ve, gate, lse, dO, dq, workspace,
                                        dtype == SWA_BF16, (hipStream_t)stream), fn);
+}
+
+int swa_bwd_dq_rowterms(const void* q, const void* k, const void* v, const void* ve,
+                        const float* gate, const int* ve_ids, int ve_rows, const int* doc_bounds,
+                        const void* o, const float* lse, const void* dO, void* dq,
+                        void* workspace, size_t ws_bytes, int B, int T, int H, int D, int window,
+                        float scale, swa_dtype dtype, void* stream) {
+  const char* fn = "swa_bwd_dq_rowterms";
+  swa::AttnShape a;
+  SWA_TRY(need(fn, "o", o));
+  // dk, dv, dve, dgate are not used by this stage; dq and lse stand in for them in the shared
+  // checks
+  SWA_TRY(check_bwd(fn, q, k, v, ve, gate, ve_ids, ve_rows, doc_bounds, o, lse, dO, dq, dq, dq,
+                    gate ? dq : nullptr, gate ? lse : nullptr, workspace, ws_bytes, B, T, H, D,
+                    window, scale, dtype, &a));
+  return hip_status(swa::launch_bwd_dq_rowterms(a, q, k, v, ve, gate, o, lse, dO, dq, workspace,
+                                                dtype == SWA_BF16, (hipStream_t)stream), fn);
 }
 
 // ---- fp8 forward variant

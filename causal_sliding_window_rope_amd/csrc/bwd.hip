@@ -606,7 +606,8 @@ hipError_t launch_bwd_dq(const AttnShape& a, const void* q, const void* k, const
                          void* dq, void* ws, bool is_bf16, hipStream_t s) {
   const int B = a.B, T = a.T, H = a.H, D = a.D;
   const WsView w = ws_view(ws, B, T, H);
-  if (is_bf16) return launch_dq_bf16(a, q, k, v, ve, gate, dO, w.nlse2, w.ndelta, dq, s);
+  if (is_bf16)
+    return launch_dq_bf16(a, q, k, v, ve, gate, dO, w.nlse2, w.ndelta, nullptr, nullptr, dq, s);
   dim3 grid(T, B * H);
   if (D == 64)
     hipLaunchKernelGGL(bwd_dq_f32_kernel<64>, grid, dim3(64), 0, s, (const float*)q, (const float*)k,
@@ -617,6 +618,18 @@ hipError_t launch_bwd_dq(const AttnShape& a, const void* q, const void* k, const
                        (const float*)v, (const float*)ve, gate, lse, w.ndelta, (const float*)dO,
                        a.bounds, a.ve_ids, a.ve_rows, (float*)dq, T, H, a.window, a.scale);
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_rowterms(const AttnShape& a, const void* q, const void* k,
+                                  const void* v, const void* ve, const float* gate,
+                                  const void* o, const float* lse, const void* dO, void* dq,
+                                  void* ws, bool is_bf16, hipStream_t s) {
+  if (!is_bf16) {
+    const hipError_t e = launch_bwd_pre(a, o, dO, lse, ws, false, s);
+    return e != hipSuccess ? e : launch_bwd_dq(a, q, k, v, ve, gate, lse, dO, dq, ws, false, s);
+  }
+  const WsView w = ws_view(ws, a.B, a.T, a.H);
+  return launch_dq_bf16(a, q, k, v, ve, gate, dO, w.nlse2, w.ndelta, o, lse, dq, s);
 }
 
 }  // namespace swa

@@ -34,7 +34,9 @@ struct Params {
   const int* bounds;   // per-token document [start, end) (document masking only)
   const int* ve_ids;   // value-embedding table rows per token (table mode only)
   int ve_rows;
-  const bf16* dO; const float* nlse2; const float* ndelta;   // row terms, negated
+  const bf16* dO;
+  float* nlse2; float* ndelta;   // row terms, negated (read; written when o is set)
+  const bf16* o; const float* lse;   // set: compute the row terms here and store them
   bf16* dq;
   int B, T, H, window, nqb;
   float c;       // scale * log2(e)
@@ -207,8 +209,31 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) dq_bf16_kernel(Params p) {
     }
   }
   const size_t rrow = (size_t)bh * T + min(myq, T - 1);
-  const float nl2 = p.nlse2[rrow];
-  const float ndl = p.ndelta[rrow];
+  float nl2, ndl;
+  if (p.o) {
+    // Row terms of this lane's query from O, dO and lse (the other half-wave holds the other
+    // dims of the row), stored for the key-major kernel that runs after this one.
+    const size_t off = head0 + (size_t)min(myq, T - 1) * H * D + 8 * hi;
+    float acc = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      float ov[8], gv[8];
+      unpack16(*reinterpret_cast<const uint4*>(p.o + off + 16 * ks), ov);
+      unpack16(__builtin_bit_cast(uint4, oreg[ks]), gv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf(ov[e], gv[e], acc);
+    }
+    acc += half_swap(acc);
+    nl2 = -p.lse[rrow] * kLog2e;
+    ndl = -acc;
+    if (hi == 0 && myq < T) {
+      p.nlse2[rrow] = nl2;
+      p.ndelta[rrow] = ndl;
+    }
+  } else {
+    nl2 = p.nlse2[rrow];
+    ndl = p.ndelta[rrow];
+  }
 
   const int qc = min(myq, T - 1);
   int start = 0;
@@ -286,12 +311,14 @@ static hipError_t launch_t(const AttnShape& a, const Params& p, hipStream_t s) {
 }  // namespace dqk
 
 hipError_t launch_dq_bf16(const AttnShape& a, const void* q, const void* k, const void* v,
-                          const void* ve, const float* gate, const void* dO, const float* nlse2,
-                          const float* ndelta, void* dq, hipStream_t s) {
+                          const void* ve, const float* gate, const void* dO, float* nlse2,
+                          float* ndelta, const void* o, const float* lse, void* dq,
+                          hipStream_t s) {
   dqk::Params p;
   p.q = (const bf16*)q; p.k = (const bf16*)k; p.v = (const bf16*)v; p.ve = (const bf16*)ve;
   p.ve_ids = a.ve_ids; p.ve_rows = a.ve_rows;
-  p.gate = gate; p.bounds = a.bounds; p.dO = (const bf16*)dO; p.nlse2 = nlse2; p.ndelta = ndelta; p.dq = (bf16*)dq;
+  p.gate = gate; p.bounds = a.bounds; p.dO = (const bf16*)dO; p.nlse2 = nlse2; p.ndelta = ndelta;
+  p.o = (const bf16*)o; p.lse = lse; p.dq = (bf16*)dq;
   p.B = a.B; p.T = a.T; p.H = a.H; p.window = a.window;
   p.nqb = (a.T + dqk::BM - 1) / dqk::BM;
   p.c = a.scale * kLog2e;

@@ -62,9 +62,16 @@ hipError_t launch_bwd_dkdv(const AttnShape& a, const void* q, const void* k, con
 hipError_t launch_bwd_dq(const AttnShape& a, const void* q, const void* k, const void* v,
                          const void* ve, const float* gate, const float* lse, const void* dO,
                          void* dq, void* ws, bool bf16, hipStream_t s);
+// dQ that also computes the row terms from O, dO and lse and stores them in the workspace
+// (bf16: inside the dQ kernel; float32: the preprocess kernel, then dQ).
+hipError_t launch_bwd_dq_rowterms(const AttnShape& a, const void* q, const void* k,
+                                  const void* v, const void* ve, const float* gate,
+                                  const void* o, const float* lse, const void* dO, void* dq,
+                                  void* ws, bool bf16, hipStream_t s);
 hipError_t launch_dq_bf16(const AttnShape& a, const void* q, const void* k, const void* v,
-                          const void* ve, const float* gate, const void* dO, const float* nlse2,
-                          const float* ndelta, void* dq, hipStream_t s);
+                          const void* ve, const float* gate, const void* dO, float* nlse2,
+                          float* ndelta, const void* o, const float* lse, void* dq,
+                          hipStream_t s);
 
 // Sliding-window decoding from a ring K/V cache (one new token per sequence).
 int decode_splits(int B, int H, int window);

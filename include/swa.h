@@ -211,8 +211,11 @@ int swa_bwd(const void* q, const void* k, const void* v, const void* ve, const f
             void* stream);
 
 /*
- * The three stages swa_bwd runs, for callers that schedule or time them separately. Call them
- * in this order on one stream with one workspace (same sizes and dtype throughout):
+ * The stages of the backward, for callers that schedule or time them separately. Both orders
+ * give the same results up to the rounding of delta (the one-call swa_bwd runs the first):
+ *   (1) swa_bwd_dq_rowterms, then swa_bwd_dkdv;
+ *   (2) swa_bwd_preprocess, then swa_bwd_dkdv and swa_bwd_dq in either order.
+ * One stream, one workspace, the same sizes and dtype throughout.
  *
  * swa_bwd_preprocess — the row terms -delta_i = -dO_i . O_i and -lse_i * log2(e) into the
  *   workspace (stored negated: the bf16 kernels start their accumulators from them).
@@ -223,7 +226,7 @@ int swa_bwd_preprocess(const void* o, const void* dO, const float* lse, void* wo
 /*
  * swa_bwd_dkdv — the key-block-major part of the recomputing backward (arguments as swa_bwd,
  *   without o and dq): writes dk, dv (and dve, dgate with the gate). Needs the workspace
- *   filled by swa_bwd_preprocess.
+ *   filled by swa_bwd_preprocess or swa_bwd_dq_rowterms.
  */
 int swa_bwd_dkdv(const void* q, const void* k, const void* v, const void* ve, const float* gate,
                  const int* ve_ids, int ve_rows, const int* doc_bounds, const float* lse,
@@ -240,6 +243,18 @@ int swa_bwd_dq(const void* q, const void* k, const void* v, const void* ve, cons
                const int* ve_ids, int ve_rows, const int* doc_bounds, const float* lse,
                const void* dO, void* dq, void* workspace, size_t ws_bytes, int B, int T, int H,
                int D, int window, float scale, swa_dtype dtype, void* stream);
+
+/*
+ * swa_bwd_dq_rowterms — swa_bwd_dq that computes the row terms itself from o, lse and dO (the
+ *   bf16 kernel: in its prologue, from the dO row it already holds and the O row) and stores
+ *   them in the workspace for a following swa_bwd_dkdv, in place of swa_bwd_preprocess.
+ *   Arguments as swa_bwd without dk, dv, dve, dgate.
+ */
+int swa_bwd_dq_rowterms(const void* q, const void* k, const void* v, const void* ve,
+                        const float* gate, const int* ve_ids, int ve_rows, const int* doc_bounds,
+                        const void* o, const float* lse, const void* dO, void* dq,
+                        void* workspace, size_t ws_bytes, int B, int T, int H, int D, int window,
+                        float scale, swa_dtype dtype, void* stream);
 
 /*
  * Sliding-window decoding from a K/V cache ("GPT-2 124M 复现" §7: generation that keeps the
