@@ -75,6 +75,15 @@ __device__ __forceinline__ void g2lds16(const void* gsrc, lds_t<bf16>* lds_base)
   __builtin_amdgcn_global_load_lds(gsrc, (lds_t<void>*)lds_base, 16, 0, 0);
 }
 
+// Per-lane 32-bit offset made opaque to the optimiser at its use, so that base + offset is
+// formed at the load (uniform 64-bit base + 32-bit lane offset) instead of being hoisted out of
+// the tile loop as a per-lane 64-bit address: the hoisted addresses cost two VGPRs each and
+// pushed the forward and dQ kernels into spilling (7-9 % of their time).
+__device__ __forceinline__ unsigned opaque(unsigned x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Wait until this wave's outstanding vector-memory operations (incl. LDS DMA) have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 

@@ -62,12 +62,12 @@ struct Tiles {
     const char* t0 = reinterpret_cast<const char*>(base + (size_t)kt * BN * rs);
     if (kt * BN + BN <= T) {
 #pragma unroll
-      for (int i = 0; i < C::NIW; ++i) g2lds16(t0 + loff[i], dst + ldst(i));
+      for (int i = 0; i < C::NIW; ++i) g2lds16(t0 + opaque(loff[i]), dst + ldst(i));
     } else {
 #pragma unroll
       for (int i = 0; i < C::NIW; ++i) {
         const int over = max(kt * BN + row(i) - (T - 1), 0);
-        g2lds16(t0 + (loff[i] - 2 * (size_t)over * rs), dst + ldst(i));
+        g2lds16(t0 + opaque(loff[i]) - 2 * (size_t)over * rs, dst + ldst(i));
       }
     }
   }

@@ -101,7 +101,8 @@ struct Tiles {
     const unsigned char* vt0 = vbase + (size_t)kt * BN;
     if (kt * BN + BN <= p.T) {
 #pragma unroll
-      for (int i = 0; i < C::KNIW; ++i) g2lds16(kt0 + koff[i], (lds_t<bf16>*)(ks + kdst[i]));
+      for (int i = 0; i < C::KNIW; ++i)
+        g2lds16(kt0 + opaque(koff[i]), (lds_t<bf16>*)(ks + kdst[i]));
     } else {
       // rows past the sequence end re-read row T-1 (their scores are masked)
 #pragma unroll
@@ -111,7 +112,8 @@ struct Tiles {
       }
     }
 #pragma unroll
-    for (int i = 0; i < C::VNIW; ++i) g2lds16(vt0 + voff[i], (lds_t<bf16>*)(vs + vdst[i]));
+    for (int i = 0; i < C::VNIW; ++i)
+      g2lds16(vt0 + opaque(voff[i]), (lds_t<bf16>*)(vs + vdst[i]));
   }
 };
 

@@ -82,14 +82,15 @@ struct Tiles {
     if (kt * BN + BN <= T) {
 #pragma unroll
       for (int i = 0; i < C::NIW; ++i) {
-        g2lds16(kt0 + loff[i], ks + ldst[i]);
-        if constexpr (!GATE) g2lds16(vt0 + loff[i], vs + ldst[i]);
+        const unsigned o = opaque(loff[i]);
+        g2lds16(kt0 + o, ks + ldst[i]);
+        if constexpr (!GATE) g2lds16(vt0 + o, vs + ldst[i]);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < C::NIW; ++i) {
         const int over = max(kt * BN + row[i] - (T - 1), 0);
-        const size_t off = loff[i] - 2 * (size_t)over * rs;
+        const size_t off = opaque(loff[i]) - 2 * (size_t)over * rs;
         g2lds16(kt0 + off, ks + ldst[i]);
         if constexpr (!GATE) g2lds16(vt0 + off, vs + ldst[i]);
       }
