@@ -338,7 +338,7 @@ def run_decode_bench(args):
     pos = torch.full((B,), p_pos, dtype=torch.int32, device="cuda")
     nws = max(sw.swa_decode_workspace_size(B, H, D, cap, max(windows)), 256)
     ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
-    P, stream = sw._ptr, sw._stream()
+    P = sw._ptr
     scale = D ** -0.5
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
@@ -348,12 +348,13 @@ def run_decode_bench(args):
             raise sw.SwaError(name, st, lib.swa_last_error().decode())
 
     def step(rec):
+        st = sw._stream()   # the current stream: the capture stream when recording a graph
         for li, t in enumerate(layers):
             call("swa_decode_prologue", P(t["q"]), P(t["k"]), P(t["v"]), P(cs), cap, P(pos),
-                 P(t["qn"]), P(t["kc"]), P(t["vc"]), B, H, D, cap, 1e-6, sw.SWA_BF16, stream)
+                 P(t["qn"]), P(t["kc"]), P(t["vc"]), B, H, D, cap, 1e-6, sw.SWA_BF16, st)
             if rec: rec[li][0].record()
             call("swa_decode", P(t["qn"]), P(t["kc"]), P(t["vc"]), P(pos), P(t["o"]), P(t["lse"]),
-                 P(ws), nws, B, H, D, cap, t["W"], scale, sw.SWA_BF16, stream)
+                 P(ws), nws, B, H, D, cap, t["W"], scale, sw.SWA_BF16, st)
             if rec: rec[li][1].record()
 
     for _ in range(args.warmup):
@@ -368,6 +369,28 @@ def run_decode_bench(args):
     torch.cuda.synchronize()
     step_ms = e0.elapsed_time(e1) / args.steps
     dec_ms = sum(r[l][0].elapsed_time(r[l][1]) for r in recs for l in range(len(layers)))
+    eager_ms = step_ms
+    if args.graph:
+        # the whole 24-layer step as one HIP graph (captured after the eager pass above, which
+        # supplies the per-kernel times); value and ms_per_step are then the replay times
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(None)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step(None)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        step_ms = e0.elapsed_time(e1) / args.steps
     launches = args.steps * len(layers)
     # algorithmic HBM bytes of the attention: W cached K and V rows per (sequence, head), the
     # query read and the output written (bf16), lse (fp32)
@@ -384,8 +407,10 @@ def run_decode_bench(args):
                                "sequences at position 2047, ring caches of 2048 slots, H=12, D=128",
                    "batch": B, "context": p_pos + 1, "parallelism": "single GPU"},
         "breakdown": {"swa_decode_ms_per_step": round(dec_ms / args.steps, 4),
-                      "prologue_ms_per_step": round(step_ms - dec_ms / args.steps, 4),
-                      "attention_bytes_per_step": total_bytes},
+                      "prologue_ms_per_step": round(eager_ms - dec_ms / args.steps, 4),
+                      "attention_bytes_per_step": total_bytes,
+                      "launch": "hip graph replay" if args.graph else "eager stream",
+                      "eager_ms_per_step": round(eager_ms, 4)},
         "roofline": {"bound": "hbm", "kernel": "decode_kernel + combine_kernel (swa_decode)",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
@@ -624,6 +649,9 @@ def main():
     ap.add_argument("--fused-gate", action="store_true",
                     help="gated workloads: form v_eff inside the attention kernels instead of "
                          "materialising it once per layer (the default, faster route)")
+    ap.add_argument("--graph", action="store_true",
+                    help="d24_decode: time the 24-layer decoding step as one captured HIP graph "
+                         "(replays) instead of eager launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="only run a plain device-to-device copy of this many MiB 5 times (used to "
