@@ -7,7 +7,9 @@
 // These kernels are HBM-bound: one row of D elements per (tensor, b, t, h) is read once and
 // written once. A row is spread over D*sizeof(E)/16 lanes so that every lane moves exactly one
 // 128-bit word; the rotation partner of lane j is lane j ^ (lanes/2) (a DPP/permute within
-// the row's lane group) and the row sum of squares is a butterfly over the same group.
+// the row's lane group) and the row sum of squares is a butterfly over the same group. In the
+// forward a wave walks the H heads of one token, which share the rotation angles; the backward
+// (two row reads per row) keeps one row per lane group, which measured faster for it.
 #include "common.h"
 #include "internal.h"
 
@@ -92,51 +94,72 @@ __device__ __forceinline__ void rotate(float* y, const float* x, const float* ot
   }
 }
 
+// Forward: one wave per (tensor, token). Its 64 / TPR row groups (TPR lanes, one 128-bit word
+// each) take consecutive heads, so each load instruction covers a contiguous run of rows, and
+// walk the H heads with stride 64 / TPR, U rows per group with their loads issued together.
+// The cos/sin of the token's position are loaded once per group for all its heads (a group per
+// row re-reads them for every head: four times as many L2 bytes as row bytes).
+constexpr int kRowsInFlight = 4;
+
 // OUT8: the normalised rows are written as e4m3 codes (scale 1; every entry of a normalised
 // row is below sqrt(D) <= 11.4 in magnitude, far inside e4m3's range, so no saturation) for
 // the fp8 forward; qn / kn then point to bytes.
 template <typename E, int D, bool OUT8>
 __global__ void __launch_bounds__(256) rope_qknorm_fwd_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const float* __restrict__ cs,
-    void* __restrict__ qn, void* __restrict__ kn, int rows_per_tensor, int T, int H, float eps) {
+    void* __restrict__ qn, void* __restrict__ kn, int tokens, int T, int H, float eps) {
   using W = RowWord<E>;
-  constexpr int VPT = W::VPT, TPR = D / VPT, HALF_T = TPR / 2;
+  constexpr int VPT = W::VPT, TPR = D / VPT, HALF_T = TPR / 2, U = kRowsInFlight;
+  constexpr int GPW = 64 / TPR;   // row groups per wave = head stride
   const int lane_in_row = threadIdx.x % TPR;
-  const int row = blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
-  if (row >= 2 * rows_per_tensor) return;  // whole row groups exit together
-  const bool is_k = row >= rows_per_tensor;
-  const int r = is_k ? row - rows_per_tensor : row;
-  const int t = (r / H) % T;
-  const size_t off = (size_t)r * D + lane_in_row * VPT;
-  W x;
-  x.load((is_k ? k : q) + off);
+  const int gw = (threadIdx.x % 64) / TPR;
+  const int wv = blockIdx.x * 4 + threadIdx.x / 64;
+  if (wv >= 2 * tokens) return;  // whole waves exit together
+  const bool is_k = wv >= tokens;
+  const int bt = is_k ? wv - tokens : wv;
+  const int t = bt % T;
+  const E* src = is_k ? k : q;
   const bool second = lane_in_row >= HALF_T;
-  float c[VPT], s[VPT], other[VPT], y[VPT];
+  float c[VPT], s[VPT];
   load_cs<VPT>(cs, t, D / 2, (lane_in_row % HALF_T) * VPT, c, s);
+  for (int h0 = gw; h0 < H; h0 += GPW * U) {
+    W x[U];
 #pragma unroll
-  for (int e = 0; e < VPT; ++e) other[e] = xor_shfl(x.v[e], HALF_T);
-  rotate<VPT>(y, x.v, other, c, s, second, 1.0f);
-  float ss = 0.f;
-#pragma unroll
-  for (int e = 0; e < VPT; ++e) ss = fmaf(y[e], y[e], ss);
-  ss = row_sum<TPR>(ss);
-  const float rinv = 1.0f / sqrtf(ss / (float)D + eps);
-  W out;
-#pragma unroll
-  for (int e = 0; e < VPT; ++e) out.v[e] = y[e] * rinv;
-  if constexpr (OUT8) {
-    unsigned w[VPT / 4];
-#pragma unroll
-    for (int j = 0; j < VPT / 4; ++j) {
-      const unsigned lo =
-          __builtin_amdgcn_cvt_pk_fp8_f32(out.v[4 * j], out.v[4 * j + 1], 0u, false);
-      w[j] = __builtin_amdgcn_cvt_pk_fp8_f32(out.v[4 * j + 2], out.v[4 * j + 3], lo, true);
+    for (int u = 0; u < U; ++u) {
+      const int h = min(h0 + GPW * u, H - 1);   // past the last head: re-read it, store nothing
+      x[u].load(src + ((size_t)bt * H + h) * D + lane_in_row * VPT);
     }
-    unsigned char* dst = static_cast<unsigned char*>(is_k ? kn : qn) + off;
-    if constexpr (VPT == 8) *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
-    else *reinterpret_cast<unsigned*>(dst) = w[0];
-  } else {
-    out.store(static_cast<E*>(is_k ? kn : qn) + off);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (h0 + GPW * u >= H) break;
+      const size_t off = ((size_t)bt * H + h0 + GPW * u) * D + lane_in_row * VPT;
+      float other[VPT], y[VPT];
+#pragma unroll
+      for (int e = 0; e < VPT; ++e) other[e] = xor_shfl(x[u].v[e], HALF_T);
+      rotate<VPT>(y, x[u].v, other, c, s, second, 1.0f);
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < VPT; ++e) ss = fmaf(y[e], y[e], ss);
+      ss = row_sum<TPR>(ss);
+      const float rinv = 1.0f / sqrtf(ss / (float)D + eps);
+      W out;
+#pragma unroll
+      for (int e = 0; e < VPT; ++e) out.v[e] = y[e] * rinv;
+      if constexpr (OUT8) {
+        unsigned w[VPT / 4];
+#pragma unroll
+        for (int j = 0; j < VPT / 4; ++j) {
+          const unsigned lo =
+              __builtin_amdgcn_cvt_pk_fp8_f32(out.v[4 * j], out.v[4 * j + 1], 0u, false);
+          w[j] = __builtin_amdgcn_cvt_pk_fp8_f32(out.v[4 * j + 2], out.v[4 * j + 3], lo, true);
+        }
+        unsigned char* dst = static_cast<unsigned char*>(is_k ? kn : qn) + off;
+        if constexpr (VPT == 8) *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+        else *reinterpret_cast<unsigned*>(dst) = w[0];
+      } else {
+        out.store(static_cast<E*>(is_k ? kn : qn) + off);
+      }
+    }
   }
 }
 
@@ -186,12 +209,10 @@ __global__ void __launch_bounds__(256) rope_qknorm_bwd_kernel(
 template <typename E, int D, bool OUT8 = false>
 static hipError_t launch_fwd_t(const void* q, const void* k, const float* cs, void* qn, void* kn,
                                int B, int T, int H, float eps, hipStream_t s) {
-  constexpr int TPR = D / (16 / sizeof(E));
-  const int rows = B * T * H;
-  const int rpb = 256 / TPR;
-  const int blocks = (2 * rows + rpb - 1) / rpb;
+  const int tokens = B * T;
+  const int blocks = (2 * tokens + 3) / 4;   // one wave per (tensor, token)
   hipLaunchKernelGGL((rope_qknorm_fwd_kernel<E, D, OUT8>), dim3(blocks), dim3(256), 0, s,
-                     (const E*)q, (const E*)k, cs, qn, kn, rows, T, H, eps);
+                     (const E*)q, (const E*)k, cs, qn, kn, tokens, T, H, eps);
   return hipGetLastError();
 }
 
