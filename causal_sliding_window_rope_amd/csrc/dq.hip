@@ -123,8 +123,10 @@ __device__ __forceinline__ void dq_tile(f32x16* dqacc, const bf16x8* qreg, const
     f32x16 s = (f32x16){}, dp = (f32x16){};
 #pragma unroll
     for (int kk = 0; kk < NKS; ++kk) {
-      const bf16x8 a = *reinterpret_cast<const lds_t<bf16x8>*>(ks + kb * 32 * D + krow[kk]);
-      const bf16x8 b = *reinterpret_cast<const lds_t<bf16x8>*>(vs + kb * 32 * D + krow[kk]);
+      const bf16x8 a = *reinterpret_cast<const lds_t<bf16x8>*>(
+          (const lds_t<char>*)ks + 2 * kb * 32 * D + krow[kk]);
+      const bf16x8 b = *reinterpret_cast<const lds_t<bf16x8>*>(
+          (const lds_t<char>*)vs + 2 * kb * 32 * D + krow[kk]);
       s = mfma32(a, qreg[kk], s);
       dp = mfma32(b, oreg[kk], dp);
     }
@@ -156,10 +158,11 @@ __device__ __forceinline__ void dq_tile(f32x16* dqacc, const bf16x8* qreg, const
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int sp = 0; sp < 2; ++sp) {
-        const int ro = (kb * 32 + sp * 16) * D;
-        const bf16x8 a = __builtin_shufflevector(ds_read_tr16(ks + ro + ktr1[db]),
-                                                 ds_read_tr16(ks + ro + ktr2[db]),
-                                                 0, 1, 2, 3, 4, 5, 6, 7);
+        const int ro = 2 * (kb * 32 + sp * 16) * D;
+        const lds_t<char>* kc = (const lds_t<char>*)ks + ro;
+        const bf16x8 a = __builtin_shufflevector(
+            ds_read_tr16((const lds_t<bf16>*)(kc + ktr1[db])),
+            ds_read_tr16((const lds_t<bf16>*)(kc + ktr2[db])), 0, 1, 2, 3, 4, 5, 6, 7);
         dqacc[db] = mfma32(a, dsb[sp], dqacc[db]);
       }
     }
@@ -249,7 +252,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) dq_bf16_kernel(Params p) {
 
   int krow[NKS];
 #pragma unroll
-  for (int kk = 0; kk < NKS; ++kk) krow[kk] = l32 * D + 8 * ((2 * kk + hi) ^ swz<D>(l32));
+  for (int kk = 0; kk < NKS; ++kk) krow[kk] = 2 * (l32 * D + 8 * ((2 * kk + hi) ^ swz<D>(l32)));
   int ktr1[NDB], ktr2[NDB];
   {
     const int g = lane >> 4, j = lane & 15;
@@ -257,8 +260,8 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) dq_bf16_kernel(Params p) {
     for (int db = 0; db < NDB; ++db) {
       const int d = 32 * db + 16 * (g & 1) + 4 * (j & 3);
       const int r1 = 4 * hi + (j >> 2), r2 = r1 + 8;
-      ktr1[db] = r1 * D + 8 * ((d >> 3) ^ swz<D>(r1)) + 4 * ((d >> 2) & 1);
-      ktr2[db] = r2 * D + 8 * ((d >> 3) ^ swz<D>(r2)) + 4 * ((d >> 2) & 1);
+      ktr1[db] = 2 * (r1 * D + 8 * ((d >> 3) ^ swz<D>(r1)) + 4 * ((d >> 2) & 1));
+      ktr2[db] = 2 * (r2 * D + 8 * ((d >> 3) ^ swz<D>(r2)) + 4 * ((d >> 2) & 1));
     }
   }
 
@@ -271,13 +274,24 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) dq_bf16_kernel(Params p) {
   tl.load(p, kbase, vbase, K0, V0, kt_lo, tid);
   wait_vmem();
   __syncthreads();
+  // The lane offsets (bytes) are redefined at every tile so that tile buffer + offset is formed
+  // at each LDS read, folded into its immediate offset, instead of being held once per buffer
+  // (which the register budget does not allow: the sums were recomputed at every read).
+  auto launder = [&]() {
+#pragma unroll
+    for (int kk = 0; kk < NKS; ++kk) asm volatile("" : "+v"(krow[kk]));
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(ktr1[db]), "+v"(ktr2[db]));
+  };
   for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
     if (kt + 1 <= kt_hi) tl.load(p, kbase, vbase, K1, V1, kt + 1, tid);
+    launder();
     dq_tile<D>(dqacc, qreg, oreg, K0, V0, krow, ktr1, ktr2, kt * BN, qw, T, lo_row, n_row, wlo0, wlo1, p.c, nl2, ndl, hi);
     wait_vmem();
     __syncthreads();
     if (kt + 1 > kt_hi) break;
     if (kt + 2 <= kt_hi) tl.load(p, kbase, vbase, K0, V0, kt + 2, tid);
+    launder();
     dq_tile<D>(dqacc, qreg, oreg, K1, V1, krow, ktr1, ktr2, (kt + 1) * BN, qw, T, lo_row, n_row, wlo0, wlo1, p.c, nl2, ndl, hi);
     wait_vmem();
     __syncthreads();
