@@ -11,7 +11,8 @@ from a seeded generator, one set per layer (kernel time does not depend on the v
 The metric counts algorithmic MFMA FLOPs only over visible (query, key) pairs: 4*D per pair
 forward, 10*D per pair backward (the five contractions of the recomputing backward).
 
-Prints one JSON line. --gpus above 1 is refused: this build runs on one GPU.
+Prints one JSON line. --gpus above 1 is refused: the benchmark measures one GPU (sharded
+over the batch, attention needs no exchange between GPUs).
 """
 
 from __future__ import annotations
@@ -696,7 +697,7 @@ def main():
                           "launches": 5}))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported; this build measures one GPU "
+        print(f"bench.py: --gpus {args.gpus} is not supported; the benchmark measures one GPU "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
     if args.workload == "d24_fwd_fp8":
