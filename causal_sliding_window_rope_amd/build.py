@@ -37,8 +37,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libswa)")
 
 
-# per-file additions (later flags win): the fp8 packing keeps NaN inputs NaN
-FILE_FLAGS = {"fp8_pack.hip": ["-fhonor-nans"]}
+# per-file additions (later flags win): the fp8 packing keeps NaN inputs NaN; decoding returns
+# NaN rows for invalid positions
+FILE_FLAGS = {"fp8_pack.hip": ["-fhonor-nans"], "decode.hip": ["-fhonor-nans"]}
 
 
 def _compile(src: str, extra: list[str]) -> str:

@@ -104,8 +104,33 @@ __device__ __forceinline__ void load16(const E* src, float* dst) {
   }
 }
 
+// Sum over the LPR lanes of a row group. Up to 16 lanes (one DPP row) by DPP adds — lane
+// swaps inside quads, then the half-row and row mirrors — with no trip through the LDS
+// crossbar; wider groups (float32 rows of 128 dims) by shuffles.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (LPR <= 16) {
+    if constexpr (LPR >= 2) x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]: lane ^ 1
+    if constexpr (LPR >= 4) x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (LPR >= 8) x += dpp_mov<0x141>(x);   // row_half_mirror: lane i <-> 7 - i
+    if constexpr (LPR >= 16) x += dpp_mov<0x140>(x);  // row_mirror: lane i <-> 15 - i
+    return x;
+  } else {
+#pragma unroll
+    for (int msk = 1; msk < LPR; msk <<= 1) x += xor_shfl(x, msk);
+    return x;
+  }
+}
+
 // one workgroup of 4 waves per (b, h, split); row group g of a wave handles every
-// (4 * RPW)-th position of the split, U positions per trip with all loads issued first
+// (4 * RPW)-th position of the split, U positions per trip: all their loads first, then the U
+// scores, then one online-softmax update for the U rows (rows past the split end, re-reading
+// the last one, get score -inf and weight 0, without a branch)
 template <typename E, int D>
 __global__ void __launch_bounds__(256) decode_kernel(Params p) {
   using C = Cfg<E, D>;
@@ -135,7 +160,9 @@ __global__ void __launch_bounds__(256) decode_kernel(Params p) {
   const size_t rs = (size_t)p.H * D;
   const size_t base = ((size_t)b * p.cap * p.H + h) * D + li * VPL;
   constexpr int STRIDE = 4 * RPW;   // positions between a group's consecutive rows
-  for (int j0 = s0 + wave * RPW + g; j0 < s1; j0 += STRIDE * U) {
+  // trip bound uniform over the wave (the groups' last trips may hold only invalid rows)
+  for (int w0 = s0 + wave * RPW; w0 < s1; w0 += STRIDE * U) {
+    const int j0 = w0 + g;
     float kv[U][VPL], vv[U][VPL];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -144,23 +171,31 @@ __global__ void __launch_bounds__(256) decode_kernel(Params p) {
       load16<E, D>(kc + off, kv[u]);
       load16<E, D>(vc + off, vv[u]);
     }
+    float d[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float d = 0.f;
+      float x = 0.f;
 #pragma unroll
-      for (int i = 0; i < VPL; ++i) d = fmaf(qv[i], kv[u][i], d);
-#pragma unroll
-      for (int msk = 1; msk < LPR; msk <<= 1) d += xor_shfl(d, msk);
-      if (j0 + u * STRIDE < s1) {   // uniform within the row group
-        const float mn = fmaxf(m, d);
-        const float a = __builtin_amdgcn_exp2f(m - mn);   // 0 while m = -inf
-        const float e = __builtin_amdgcn_exp2f(d - mn);
-        l = l * a + e;
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) acc[i] = fmaf(acc[i], a, e * vv[u][i]);
-        m = mn;
-      }
+      for (int i = 0; i < VPL; ++i) x = fmaf(qv[i], kv[u][i], x);
+      x = group_sum<LPR>(x);
+      d[u] = (j0 + u * STRIDE < s1) ? x : -INFINITY;
     }
+    float mn = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mn = fmaxf(mn, d[u]);
+    const float ms = (mn == -INFINITY) ? 0.f : mn;   // all -inf so far: every weight is 0
+    const float a = __builtin_amdgcn_exp2f(m - ms);
+    l *= a;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) acc[i] *= a;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float e = __builtin_amdgcn_exp2f(d[u] - ms);
+      l += e;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) acc[i] = fmaf(e, vv[u][i], acc[i]);
+    }
+    m = mn;
   }
   // merge the row groups of the wave (lanes li, li + LPR, ...), then the four waves via LDS
 #pragma unroll
