@@ -57,6 +57,28 @@ __device__ __forceinline__ uint4 pack16(const float (&v)[8]) {
 // Wave64 cross-lane helpers.
 __device__ __forceinline__ float xor_shfl(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// Lane exchange inside a DPP row of 16 lanes (no trip through the LDS crossbar that
+// xor_shfl takes). CTRL: 0xB1 quad_perm [1,0,3,2] (lane ^ 1), 0x4E quad_perm [2,3,0,1]
+// (lane ^ 2), 0x141 row_half_mirror (i <-> 7 - i), 0x140 row_mirror (i <-> 15 - i), 0x128
+// row_ror:8 (lane ^ 8 within the row).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of N lanes (N a power of two <= 64): DPP adds up to a 16-lane row
+// (quad swaps, then the half-row and row mirrors), shuffles beyond.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp_mov<0xB1>(x);
+  if constexpr (N >= 4) x += dpp_mov<0x4E>(x);
+  if constexpr (N >= 8) x += dpp_mov<0x141>(x);
+  if constexpr (N >= 16) x += dpp_mov<0x140>(x);
+#pragma unroll
+  for (int m = 16; m < N; m <<= 1) x += xor_shfl(x, m);
+  return x;
+}
+
 // max / sum over the two 32-lane halves of a wave (lane l and lane l^32).
 __device__ __forceinline__ float half_swap(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);

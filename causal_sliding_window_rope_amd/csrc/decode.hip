@@ -104,29 +104,6 @@ __device__ __forceinline__ void load16(const E* src, float* dst) {
   }
 }
 
-// Sum over the LPR lanes of a row group. Up to 16 lanes (one DPP row) by DPP adds — lane
-// swaps inside quads, then the half-row and row mirrors — with no trip through the LDS
-// crossbar; wider groups (float32 rows of 128 dims) by shuffles.
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-
-template <int LPR>
-__device__ __forceinline__ float group_sum(float x) {
-  if constexpr (LPR <= 16) {
-    if constexpr (LPR >= 2) x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]: lane ^ 1
-    if constexpr (LPR >= 4) x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]: lane ^ 2
-    if constexpr (LPR >= 8) x += dpp_mov<0x141>(x);   // row_half_mirror: lane i <-> 7 - i
-    if constexpr (LPR >= 16) x += dpp_mov<0x140>(x);  // row_mirror: lane i <-> 15 - i
-    return x;
-  } else {
-#pragma unroll
-    for (int msk = 1; msk < LPR; msk <<= 1) x += xor_shfl(x, msk);
-    return x;
-  }
-}
-
 // one workgroup of 4 waves per (b, h, split); row group g of a wave handles every
 // (4 * RPW)-th position of the split, U positions per trip: all their loads first, then the U
 // scores, then one online-softmax update for the U rows (rows past the split end, re-reading
@@ -177,7 +154,7 @@ __global__ void __launch_bounds__(256) decode_kernel(Params p) {
       float x = 0.f;
 #pragma unroll
       for (int i = 0; i < VPL; ++i) x = fmaf(qv[i], kv[u][i], x);
-      x = group_sum<LPR>(x);
+      x = group_sum<LPR>(x);   // DPP adds within a 16-lane row
       d[u] = (j0 + u * STRIDE < s1) ? x : -INFINITY;
     }
     float mn = m;

@@ -64,9 +64,15 @@ template <typename E> struct RowWord {
 // Sum over the TPR lanes that hold one row (TPR is a power of two <= 64, groups aligned).
 template <int TPR>
 __device__ __forceinline__ float row_sum(float x) {
-#pragma unroll
-  for (int m = 1; m < TPR; m <<= 1) x += xor_shfl(x, m);
-  return x;
+  return group_sum<TPR>(x);
+}
+
+// The rotation partner's value: lane j ^ (TPR/2) of the row group (a DPP row rotation for
+// 16-lane groups, a shuffle otherwise).
+template <int TPR>
+__device__ __forceinline__ float partner(float x) {
+  if constexpr (TPR == 16) return dpp_mov<0x128>(x);
+  else return xor_shfl(x, TPR / 2);
 }
 
 // cos/sin of the VPT angle slots starting at pair index i0 for position t.
@@ -135,7 +141,7 @@ __global__ void __launch_bounds__(256) rope_qknorm_fwd_kernel(
       const size_t off = ((size_t)bt * H + h0 + GPW * u) * D + lane_in_row * VPT;
       float other[VPT], y[VPT];
 #pragma unroll
-      for (int e = 0; e < VPT; ++e) other[e] = xor_shfl(x[u].v[e], HALF_T);
+      for (int e = 0; e < VPT; ++e) other[e] = partner<TPR>(x[u].v[e]);
       rotate<VPT>(y, x[u].v, other, c, s, second, 1.0f);
       float ss = 0.f;
 #pragma unroll
@@ -184,7 +190,7 @@ __global__ void __launch_bounds__(256) rope_qknorm_bwd_kernel(
   float c[VPT], s[VPT], other[VPT], u[VPT];
   load_cs<VPT>(cs, t, D / 2, (lane_in_row % HALF_T) * VPT, c, s);
 #pragma unroll
-  for (int e = 0; e < VPT; ++e) other[e] = xor_shfl(x.v[e], HALF_T);
+  for (int e = 0; e < VPT; ++e) other[e] = partner<TPR>(x.v[e]);
   rotate<VPT>(u, x.v, other, c, s, second, 1.0f);
   float ss = 0.f;
 #pragma unroll
@@ -200,7 +206,7 @@ __global__ void __launch_bounds__(256) rope_qknorm_bwd_kernel(
 #pragma unroll
   for (int e = 0; e < VPT; ++e) du[e] = rinv * (g.v[e] - u[e] * rinv * dd);
 #pragma unroll
-  for (int e = 0; e < VPT; ++e) other[e] = xor_shfl(du[e], HALF_T);
+  for (int e = 0; e < VPT; ++e) other[e] = partner<TPR>(du[e]);
   W out;
   rotate<VPT>(out.v, du, other, c, s, second, -1.0f);
   out.store((is_k ? dk : dq) + off);
