@@ -102,8 +102,7 @@ __global__ void __launch_bounds__(256) gate_dv_kernel(const E* __restrict__ dv,
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < VPT; ++i) s = fmaf(a[i], e[i], s);
-#pragma unroll
-  for (int m = WPR / 2; m > 0; m >>= 1) s += xor_shfl(s, m);
+  s = group_sum<WPR>(s);   // DPP adds within a 16-lane row
   if (!ok) return;
   if (c == 0) dgate[r] = s;
   if (!ids) {
