@@ -65,7 +65,7 @@ __global__ void __launch_bounds__(256) vpack_kernel(const E* __restrict__ v,
   constexpr int RS = D + 4;    // LDS row stride in bytes
   __shared__ unsigned tile32[64 * RS / 4];
   unsigned char* tile = reinterpret_cast<unsigned char*>(tile32);
-  const int kt = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh - b * H;
+  const int kt = blockIdx.y, bh = blockIdx.x, b = bh / H, h = bh - b * H;
   constexpr int CPR = D / 8;   // 8-element chunks per key row
   for (int i = threadIdx.x; i < 64 * CPR; i += 256) {
     const int key = i / CPR, c = i - key * CPR;
@@ -126,7 +126,7 @@ template <typename E>
 static void vpack_t(const void* v, void* v8t, float inv, int B, int T, int H, int D,
                     hipStream_t s) {
   const int Tp = (T + 63) / 64 * 64;
-  const dim3 grid(Tp / 64, B * H);
+  const dim3 grid(B * H, Tp / 64);   // the heads of one key block in neighbouring workgroups
   if (D == 64)
     hipLaunchKernelGGL((f8p::vpack_kernel<E, 64>), grid, dim3(256), 0, s, (const E*)v,
                        (uint4*)v8t, inv, T, H, Tp);
