@@ -103,20 +103,36 @@ __device__ __forceinline__ void load_qtile(const Params& p, const bf16* qbase, c
                                            lds_t<float>* Dls, int qt, int wave, int lane) {
   using C = Cfg<D>;
   const size_t rs = (size_t)p.H * D;
+  // buffer copies relative to the tile's first row (32-bit lane offsets within one tile)
+  const size_t t0 = (size_t)qt * BMQ * rs;
+  const __amdgpu_buffer_rsrc_t rq = buf_rsrc(qbase + t0), ro = buf_rsrc(obase + t0);
 #pragma unroll
   for (int i = 0; i < C::NIQ; ++i) {
     const int I = wave * C::NIQ + i;
     const int r = I * C::RPI + lane / C::CH;
     const int c = (lane % C::CH) ^ swz<D>(r);
-    const size_t goff = (size_t)min(qt * BMQ + r, p.T - 1) * rs + 8 * c;
-    g2lds16(qbase + goff, Qs + I * C::RPI * D);
-    g2lds16(obase + goff, Os + I * C::RPI * D);
+    const unsigned vo = 2u * ((unsigned)(min(qt * BMQ + r, p.T - 1) - qt * BMQ) * (unsigned)rs +
+                              8u * c);
+    b2lds16(rq, vo, (lds_t<void>*)(Qs + I * C::RPI * D));
+    b2lds16(ro, vo, (lds_t<void>*)(Os + I * C::RPI * D));
   }
-  if (lane < BMQ / 4) {
+  if (lane < BMQ / 4 && wave < 2) {
     // a tile that runs past the sequence end reads into the next head's row or the workspace
     // slack (see bwd_workspace_bytes); those queries are masked
-    if (wave == 0) g2lds16(l2base + qt * BMQ + 4 * lane, (lds_t<bf16>*)Ls);
-    if (wave == 1) g2lds16(dlbase + qt * BMQ + 4 * lane, (lds_t<bf16>*)Dls);
+    const __amdgpu_buffer_rsrc_t rl = buf_rsrc((wave == 0 ? l2base : dlbase) + qt * BMQ);
+    b2lds16(rl, 16u * lane, (lds_t<void>*)(wave == 0 ? Ls : Dls));
+  }
+}
+
+// Scheduling of the S MFMAs of one 32-query unit (NKS of them) with the 4 + NKS LDS reads of
+// the dP operands written after them: each MFMA is followed by two reads while more reads than
+// MFMAs remain, then by one.
+template <int NKS, int I = 0>
+__device__ __forceinline__ void mfma_ds_interleave() {
+  if constexpr (I < NKS) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, I < 4 ? 2 : 1, 0);      // LDS reads
+    mfma_ds_interleave<NKS, I + 1>();
   }
 }
 
@@ -239,35 +255,38 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dkdv_bf16_kernel(Params 
       const bool need_mask = (qm < kw + 31) || (qm + 31 > whi0) || (qm + 32 > T) ||
                              (kw + 32 > T);
       // The LDS operands of each phase are requested together, one phase ahead where registers
-      // allow, so the reads overlap one another and the MFMAs of the previous phase; the waits
-      // before the MFMAs then count down instead of draining the LDS queue each time.
+      // allow, so the reads overlap one another and the MFMAs of the previous phase. The S
+      // operands (row term, Q) come first and the dP operands (row term, dO) are issued between
+      // the S MFMAs: with at most 12 reads in flight at the first MFMA, the waits count down.
+      // S' = -lse2 + c Q K^T and dP' = -delta + dO V^T (lane = key, 16 queries per lane): the
+      // accumulators start from the negated row terms of their 16 queries.
+      f32x4 l2v[4], dlv[4];
       bf16x8 aq[NKS], ao[NKS];
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const int off = mb * 32 * D + rowb[ks];
-        aq[ks] = *reinterpret_cast<const lds_t<bf16x8>*>(Qs + off);
-        ao[ks] = *reinterpret_cast<const lds_t<bf16x8>*>(Os + off);
-      }
-      f32x4 l2v[4], dlv[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
+      for (int a = 0; a < 4; ++a)
         l2v[a] = *reinterpret_cast<const lds_t<f32x4>*>(Ls + mb * 32 + 8 * a + 4 * hi);
-        dlv[a] = *reinterpret_cast<const lds_t<f32x4>*>(Dls + mb * 32 + 8 * a + 4 * hi);
-      }
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        aq[ks] = *reinterpret_cast<const lds_t<bf16x8>*>(Qs + mb * 32 * D + rowb[ks]);
       sched_fence();
-      // S' = -lse2 + c Q K^T and dP' = -delta + dO V^T (lane = key, 16 queries per lane): the
-      // accumulators start from the negated row terms of their 16 queries
       f32x16 s = __builtin_shufflevector(__builtin_shufflevector(l2v[0], l2v[1], 0, 1, 2, 3, 4, 5, 6, 7),
                                          __builtin_shufflevector(l2v[2], l2v[3], 0, 1, 2, 3, 4, 5, 6, 7),
                                          0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) s = mfma32(aq[ks], kreg[ks], s);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        dlv[a] = *reinterpret_cast<const lds_t<f32x4>*>(Dls + mb * 32 + 8 * a + 4 * hi);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        ao[ks] = *reinterpret_cast<const lds_t<bf16x8>*>(Os + mb * 32 * D + rowb[ks]);
+      mfma_ds_interleave<NKS>();
+      sched_fence();
       f32x16 dp = __builtin_shufflevector(__builtin_shufflevector(dlv[0], dlv[1], 0, 1, 2, 3, 4, 5, 6, 7),
                                           __builtin_shufflevector(dlv[2], dlv[3], 0, 1, 2, 3, 4, 5, 6, 7),
                                           0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        s = mfma32(aq[ks], kreg[ks], s);
-        dp = mfma32(ao[ks], vreg[ks], dp);
-      }
+      for (int ks = 0; ks < NKS; ++ks) dp = mfma32(ao[ks], vreg[ks], dp);
       // B operands of dV += P^T dO by transposing reads of the row-major dO tile
       bf16x8 bo[NDB][2];
 #pragma unroll

@@ -91,14 +91,23 @@ template <typename T> using lds_t = __attribute__((address_space(3))) T;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-// Asynchronous 16-byte global -> LDS copy: lane l of the wave writes lds_base + 16*l bytes
-// (lds_base must be the same for the whole wave).
-__device__ __forceinline__ void g2lds16(const void* gsrc, lds_t<bf16>* lds_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (lds_t<void>*)lds_base, 16, 0, 0);
+// Asynchronous 16-byte global -> LDS copy in its buffer form (buffer_load_dwordx4 ... lds):
+// lane l of the wave reads resource + voff bytes and writes lds_base + 16*l bytes (lds_base
+// must be the same for the whole wave). The resource is a uniform base address with a range of
+// 2^31 - 1 bytes and the raw-buffer configuration word of gfx9-family targets. The compiler
+// counts these copies on vmcnt alone; the global form (global_load_lds) it also treats as a
+// possible LDS access, which makes every LDS read issued while a copy is in flight wait for
+// lgkmcnt(0) instead of for its own place in the queue (3-5 % of the dK/dV kernel's time).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ void b2lds16(__amdgpu_buffer_rsrc_t r, unsigned voff,
+                                        lds_t<void>* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, voff, 0, 0, 0);
 }
 
 // Per-lane 32-bit offset made opaque to the optimiser at its use, so that base + offset is
-// formed at the load (uniform 64-bit base + 32-bit lane offset) instead of being hoisted out of
+// formed at the load (uniform base + 32-bit lane offset) instead of being hoisted out of
 // the tile loop as a per-lane 64-bit address: the hoisted addresses cost two VGPRs each and
 // pushed the forward and dQ kernels into spilling (7-9 % of their time).
 __device__ __forceinline__ unsigned opaque(unsigned x) {

@@ -59,15 +59,16 @@ struct Tiles {
   }
   __device__ __forceinline__ void load_rows(const bf16* base, lds_t<bf16>* dst, int kt, int T,
                                             size_t rs) const {
-    const char* t0 = reinterpret_cast<const char*>(base + (size_t)kt * BN * rs);
+    const __amdgpu_buffer_rsrc_t r = buf_rsrc(base + (size_t)kt * BN * rs);
     if (kt * BN + BN <= T) {
 #pragma unroll
-      for (int i = 0; i < C::NIW; ++i) g2lds16(t0 + opaque(loff[i]), dst + ldst(i));
+      for (int i = 0; i < C::NIW; ++i) b2lds16(r, opaque(loff[i]), (lds_t<void>*)(dst + ldst(i)));
     } else {
 #pragma unroll
       for (int i = 0; i < C::NIW; ++i) {
         const int over = max(kt * BN + row(i) - (T - 1), 0);
-        g2lds16(t0 + opaque(loff[i]) - 2 * (size_t)over * rs, dst + ldst(i));
+        b2lds16(r, opaque(loff[i]) - 2u * (unsigned)over * (unsigned)rs,
+                (lds_t<void>*)(dst + ldst(i)));
       }
     }
   }

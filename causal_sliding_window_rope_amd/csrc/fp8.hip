@@ -97,23 +97,23 @@ struct Tiles {
                                        const unsigned char* vbase, lds_t<unsigned char>* ks,
                                        lds_t<unsigned char>* vs, int kt) const {
     const size_t rs = (size_t)p.H * D;
-    const unsigned char* kt0 = kbase + (size_t)kt * BN * rs;
-    const unsigned char* vt0 = vbase + (size_t)kt * BN;
+    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kbase + (size_t)kt * BN * rs);
+    const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vbase + (size_t)kt * BN);
     if (kt * BN + BN <= p.T) {
 #pragma unroll
       for (int i = 0; i < C::KNIW; ++i)
-        g2lds16(kt0 + opaque(koff[i]), (lds_t<bf16>*)(ks + kdst[i]));
+        b2lds16(rk, opaque(koff[i]), (lds_t<void>*)(ks + kdst[i]));
     } else {
       // rows past the sequence end re-read row T-1 (their scores are masked)
 #pragma unroll
       for (int i = 0; i < C::KNIW; ++i) {
         const int over = max(kt * BN + krow[i] - (p.T - 1), 0);
-        g2lds16(kt0 + koff[i] - (size_t)over * rs, (lds_t<bf16>*)(ks + kdst[i]));
+        b2lds16(rk, koff[i] - (unsigned)over * (unsigned)rs, (lds_t<void>*)(ks + kdst[i]));
       }
     }
 #pragma unroll
     for (int i = 0; i < C::VNIW; ++i)
-      g2lds16(vt0 + opaque(voff[i]), (lds_t<bf16>*)(vs + vdst[i]));
+      b2lds16(rv, opaque(voff[i]), (lds_t<void>*)(vs + vdst[i]));
   }
 };
 

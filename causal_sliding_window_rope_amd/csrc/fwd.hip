@@ -71,28 +71,28 @@ struct Tiles {
       ldst[i] = I * C::RPI * D;
     }
   }
-  // Issue the loads of key tile kt into (ks, vs): uniform 64-bit tile base + 32-bit lane offset.
+  // Issue the loads of key tile kt into (ks, vs): buffer resource at the tile base + 32-bit lane offset.
   // In the last tile, rows past the sequence end re-read row T-1 (their scores are masked).
   __device__ __forceinline__ void load(const Params& p, const bf16* kbase, const bf16* vbase,
                                        lds_t<bf16>* ks, lds_t<bf16>* vs, int kt, int tid) const {
     const int T = p.T;
     const size_t rs = (size_t)p.H * D;
-    const char* kt0 = reinterpret_cast<const char*>(kbase + (size_t)kt * BN * rs);
-    const char* vt0 = reinterpret_cast<const char*>(vbase + (size_t)kt * BN * rs);
+    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kbase + (size_t)kt * BN * rs);
+    const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vbase + (size_t)kt * BN * rs);
     if (kt * BN + BN <= T) {
 #pragma unroll
       for (int i = 0; i < C::NIW; ++i) {
         const unsigned o = opaque(loff[i]);
-        g2lds16(kt0 + o, ks + ldst[i]);
-        if constexpr (!GATE) g2lds16(vt0 + o, vs + ldst[i]);
+        b2lds16(rk, o, (lds_t<void>*)(ks + ldst[i]));
+        if constexpr (!GATE) b2lds16(rv, o, (lds_t<void>*)(vs + ldst[i]));
       }
     } else {
 #pragma unroll
       for (int i = 0; i < C::NIW; ++i) {
         const int over = max(kt * BN + row[i] - (T - 1), 0);
-        const size_t off = opaque(loff[i]) - 2 * (size_t)over * rs;
-        g2lds16(kt0 + off, ks + ldst[i]);
-        if constexpr (!GATE) g2lds16(vt0 + off, vs + ldst[i]);
+        const unsigned off = opaque(loff[i]) - 2u * (unsigned)over * (unsigned)rs;
+        b2lds16(rk, off, (lds_t<void>*)(ks + ldst[i]));
+        if constexpr (!GATE) b2lds16(rv, off, (lds_t<void>*)(vs + ldst[i]));
       }
     }
     if constexpr (GATE) {
