@@ -124,15 +124,15 @@ __device__ __forceinline__ void load_qtile(const Params& p, const bf16* qbase, c
   }
 }
 
-// Scheduling of the S MFMAs of one 32-query unit (NKS of them) with the 4 + NKS LDS reads of
-// the dP operands written after them: each MFMA is followed by two reads while more reads than
-// MFMAs remain, then by one.
-template <int NKS, int I = 0>
+// Scheduling of N MFMAs with the LDS reads written after them (a row term and the operand rows
+// of one 32-query unit, 4 + N reads when N = D / 16): each MFMA is followed by two reads for the
+// first four, then by one.
+template <int N, int I = 0>
 __device__ __forceinline__ void mfma_ds_interleave() {
-  if constexpr (I < NKS) {
+  if constexpr (I < N) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // one MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, I < 4 ? 2 : 1, 0);      // LDS reads
-    mfma_ds_interleave<NKS, I + 1>();
+    mfma_ds_interleave<N, I + 1>();
   }
 }
 
@@ -247,27 +247,38 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dkdv_bf16_kernel(Params 
   auto tile = [&](const lds_t<bf16>* Qs, const lds_t<bf16>* Os, const lds_t<float>* Ls,
                   const lds_t<float>* Dls, int qt) {
     const int q0 = qt * BMQ;
-#pragma unroll
-    for (int mb = 0; mb < BMQ / 32; ++mb) {
-      const int qm = q0 + 32 * mb;
-      const bool skip = (qm + 31 < kw) || (qm > whi1) || (kw >= T);
-      if (skip) continue;
-      const bool need_mask = (qm < kw + 31) || (qm + 31 > whi0) || (qm + 32 > T) ||
-                             (kw + 32 > T);
-      // The LDS operands of each phase are requested together, one phase ahead where registers
-      // allow, so the reads overlap one another and the MFMAs of the previous phase. The S
-      // operands (row term, Q) come first and the dP operands (row term, dO) are issued between
-      // the S MFMAs: with at most 12 reads in flight at the first MFMA, the waits count down.
-      // S' = -lse2 + c Q K^T and dP' = -delta + dO V^T (lane = key, 16 queries per lane): the
-      // accumulators start from the negated row terms of their 16 queries.
-      f32x4 l2v[4], dlv[4];
-      bf16x8 aq[NKS], ao[NKS];
+    // S operands of a unit (row term, Q rows): read for unit 0 here and for unit mb + 1 during
+    // the dK MFMAs of unit mb
+    f32x4 l2v[4];
+    bf16x8 aq[NKS];
+    auto read_s_ops = [&](int mb) __attribute__((always_inline)) {
 #pragma unroll
       for (int a = 0; a < 4; ++a)
         l2v[a] = *reinterpret_cast<const lds_t<f32x4>*>(Ls + mb * 32 + 8 * a + 4 * hi);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
         aq[ks] = *reinterpret_cast<const lds_t<bf16x8>*>(Qs + mb * 32 * D + rowb[ks]);
+    };
+    read_s_ops(0);
+#pragma unroll
+    for (int mb = 0; mb < BMQ / 32; ++mb) {
+      const int qm = q0 + 32 * mb;
+      const bool skip = (qm + 31 < kw) || (qm > whi1) || (kw >= T);
+      if (skip) {
+        if (mb + 1 < BMQ / 32) read_s_ops(mb + 1);
+        continue;
+      }
+      const bool need_mask = (qm < kw + 31) || (qm + 31 > whi0) || (qm + 32 > T) ||
+                             (kw + 32 > T);
+      // The LDS operands of each phase are requested one phase ahead, so the reads overlap one
+      // another and the MFMAs of the previous phase: the S operands (row term, Q) during the
+      // previous unit's dK MFMAs, the dP operands (row term, dO) between the S MFMAs, the dV
+      // operands during the dP MFMAs, the dK operands during the dV MFMAs. LDS reads complete
+      // in order, so each MFMA waits only for its own operand.
+      // S' = -lse2 + c Q K^T and dP' = -delta + dO V^T (lane = key, 16 queries per lane): the
+      // accumulators start from the negated row terms of their 16 queries.
+      f32x4 dlv[4];
+      bf16x8 ao[NKS];
       sched_fence();
       f32x16 s = __builtin_shufflevector(__builtin_shufflevector(l2v[0], l2v[1], 0, 1, 2, 3, 4, 5, 6, 7),
                                          __builtin_shufflevector(l2v[2], l2v[3], 0, 1, 2, 3, 4, 5, 6, 7),
@@ -281,6 +292,9 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dkdv_bf16_kernel(Params 
       for (int ks = 0; ks < NKS; ++ks)
         ao[ks] = *reinterpret_cast<const lds_t<bf16x8>*>(Os + mb * 32 * D + rowb[ks]);
       mfma_ds_interleave<NKS>();
+      // The MFMA builtins carry no order: without this use of S here, instruction selection
+      // may place the last S MFMA behind the dP chain, and the exp2 of S then waits for dP.
+      asm volatile("" : "+a"(s));
       sched_fence();
       f32x16 dp = __builtin_shufflevector(__builtin_shufflevector(dlv[0], dlv[1], 0, 1, 2, 3, 4, 5, 6, 7),
                                           __builtin_shufflevector(dlv[2], dlv[3], 0, 1, 2, 3, 4, 5, 6, 7),
@@ -353,11 +367,15 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dkdv_bf16_kernel(Params 
         sbf[a >> 1][e0 + 2] = d23[0]; sbf[a >> 1][e0 + 3] = d23[1];
       }
       sched_fence();
-      // dK += dS^T Q
+      // dK += dS^T Q, with the next unit's S operands read between the MFMAs
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int sp = 0; sp < 2; ++sp) dk[db] = mfma32(sbf[sp], bq[db][sp], dk[db]);
+      if (mb + 1 < BMQ / 32) {
+        read_s_ops(mb + 1);
+        mfma_ds_interleave<2 * NDB>();
+      }
       sched_fence();
     }
   };
