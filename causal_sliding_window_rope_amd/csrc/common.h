@@ -94,7 +94,8 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 // Asynchronous 16-byte global -> LDS copy in its buffer form (buffer_load_dwordx4 ... lds):
 // lane l of the wave reads resource + voff bytes and writes lds_base + 16*l bytes (lds_base
 // must be the same for the whole wave). The resource is a uniform base address with a range of
-// 2^31 - 1 bytes and the raw-buffer configuration word of gfx9-family targets. The compiler
+// 2^31 - 1 bytes (every offset from a tile's first row stays below it: the entry points cap a
+// tensor at 2^30 elements) and the raw-buffer configuration word of gfx9-family targets. The compiler
 // counts these copies on vmcnt alone; the global form (global_load_lds) it also treats as a
 // possible LDS access, which makes every LDS read issued while a copy is in flight wait for
 // lgkmcnt(0) instead of for its own place in the queue (3-5 % of the dK/dV kernel's time).
