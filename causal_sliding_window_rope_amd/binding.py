@@ -296,6 +296,32 @@ def swa_bwd(q, k, v, o, lse, dO, window: int, scale: float | None = None, ve=Non
     return dq, dk, dv
 
 
+def rowterm_views(workspace, B: int, T: int, H: int):
+    """(ndelta, nlse2) float32 (B, H, T) views of a swa_bwd workspace: the row terms -delta and
+    -lse*log2(e) as the header lays them out (each array 256-byte aligned, then 512 bytes of
+    slack)."""
+    n = B * H * T
+    blk = ((n * 4 + 255) // 256) * 256 + 512
+    f = workspace.view(torch.uint8)
+    nd = f[:n * 4].view(torch.float32).view(B, H, T)
+    nl = f[blk:blk + n * 4].view(torch.float32).view(B, H, T)
+    return nd, nl
+
+
+def swa_bwd_preprocess(o, dO, lse, workspace=None):
+    """Row terms of the backward into a (new or given) workspace; returns the workspace."""
+    B, T, H, D = o.shape
+    _check(o, "o", (B, T, H, D))
+    _check(dO, "dO", (B, T, H, D), o.dtype)
+    _check(lse, "lse", (B, H, T), torch.float32)
+    ws_bytes = swa_bwd_workspace_size(B, T, H, D, o.dtype)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=o.device)
+    _call("swa_bwd_preprocess", _ptr(o), _ptr(dO), _ptr(lse), _ptr(workspace),
+          workspace.numel() * workspace.element_size(), B, T, H, D, _dt(o), _stream())
+    return workspace
+
+
 def swa_bwd_stages(q, k, v, o, lse, dO, window: int, scale: float | None = None, ve=None,
                    gate=None, workspace=None, grads=None, doc_bounds=None, ve_ids=None,
                    preprocess: bool = False):

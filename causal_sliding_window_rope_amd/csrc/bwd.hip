@@ -29,6 +29,9 @@ namespace swa {
 // ------------------------------------------------------------------------------------------
 // ndelta_i = -sum_d dO[i, d] * O[i, d] and nlse2_i = -lse_i * log2(e), both (B, H, T).
 // ------------------------------------------------------------------------------------------
+// Rows of slack zeroed behind each row-term array (a query tile is 128 rows).
+constexpr int kRowTermSlackRows = 128;
+
 template <typename E, int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(const E* __restrict__ o,
                                                       const E* __restrict__ dO,
@@ -39,7 +42,13 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const E* __restrict__ o,
   constexpr int VPT = 16 / sizeof(E), TPR = D / VPT;
   const int lr = threadIdx.x % TPR;
   const int row = blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
-  if (row >= rows) return;
+  if (row >= rows) {
+    // The 128-query tiles of the bf16 dK/dV kernel read the row terms of the last head up to
+    // 127 rows past its end, in the slack behind each array: zero them, so that a workspace
+    // holding NaN or Inf bit patterns cannot reach dS = P (dP - delta) of a masked query.
+    if (row < rows + kRowTermSlackRows && lr == 0) { ndelta[row] = 0.f; nlse2[row] = 0.f; }
+    return;
+  }
   const size_t off = (size_t)row * D + lr * VPT;
   const uint4 a = *reinterpret_cast<const uint4*>(o + off);
   const uint4 g = *reinterpret_cast<const uint4*>(dO + off);
@@ -545,7 +554,8 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace: -delta (B,H,T) | -lse*log2(e) (B,H,T), float32. Each block is 256-byte aligned and followed
 // by 512 bytes of slack, so the 16-byte row-term loads of a query tile that runs past the
-// sequence end stay inside the allocation.
+// sequence end stay inside the allocation; the kernels that write the row terms also write
+// zeros to the first 128 slack rows (the only ones such a tile reads).
 static size_t rowterm_block(int B, int T, int H) {
   return align256((size_t)B * H * T * sizeof(float)) + 512;
 }
@@ -562,7 +572,8 @@ static void launch_pre(const void* o, const void* dO, const float* lse, float* n
   constexpr int TPR = D / (16 / sizeof(E));
   const int rows = B * T * H;
   const int rpb = 256 / TPR;
-  hipLaunchKernelGGL((bwd_pre_kernel<E, D>), dim3((rows + rpb - 1) / rpb), dim3(256), 0, s,
+  const int span = rows + kRowTermSlackRows;   // the rows, then the zeroed slack
+  hipLaunchKernelGGL((bwd_pre_kernel<E, D>), dim3((span + rpb - 1) / rpb), dim3(256), 0, s,
                      (const E*)o, (const E*)dO, lse, ndelta, nlse2, rows, T, H);
 }
 

@@ -233,6 +233,12 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) dq_bf16_kernel(Params p) {
     if (hi == 0 && myq < T) {
       p.nlse2[rrow] = nl2;
       p.ndelta[rrow] = ndl;
+    } else if (hi == 0 && bh == p.B * H - 1) {
+      // past the end of the last head: the slack rows the dK/dV kernel's last query tile
+      // reads (masked queries) are zeroed, so no bit pattern left in the workspace reaches dS
+      const size_t tail = (size_t)bh * T + myq;
+      p.nlse2[tail] = 0.f;
+      p.ndelta[tail] = 0.f;
     }
   } else {
     nl2 = p.nlse2[rrow];

@@ -2,9 +2,9 @@
 //
 // Method: as the bf16 forward ("GPT-2 124M 复现" §3 and §19: scaled scores, causal window,
 // online softmax, P V), with both contractions on v_mfma_f32_32x32x64_f8f6f4. fp8 follows
-// "从4万美元到73美元" (intelliparadigm.com), the paragraph on mixed precision: an 8-bit
-// floating-point format that doubles matrix throughput over bf16 and needs scales
-// (calibration). Each of q_hat, k_hat, v carries one float32 scale; scores and probabilities
+// "NanoGPT Speedrun：大模型训练效率的极限竞速指南" (kongchang.com), section "工程与硬件优化",
+// its paragraph on bf16 and fp8: an 8-bit floating-point format that can double matrix
+// throughput over bf16 and needs finer calibration (scales). Each of q_hat, k_hat, v carries one float32 scale; scores and probabilities
 // stay in float32, P is rounded to e4m3 as the PV operand (as the bf16 kernels round it to
 // bf16), and O is written in bf16.
 //

@@ -1,7 +1,8 @@
 // Packing of q, k, v into the e4m3 operands of the fp8 forward (fp8.hip).
 //
-// Format and calibration ("从4万美元到73美元", intelliparadigm.com, the paragraph on mixed
-// precision: fp8 needs scales to stay accurate): OCP e4m3, one float32 scale per tensor,
+// Format and calibration ("NanoGPT Speedrun：大模型训练效率的极限竞速指南", kongchang.com,
+// section "工程与硬件优化", its paragraph on bf16 and fp8: fp8 needs finer calibration to stay
+// accurate): OCP e4m3, one float32 scale per tensor,
 // code = e4m3(x * (1/scale)) with one float32 multiply and one nearest-even rounding,
 // saturating finite values beyond 448 (the conversion instruction itself would give NaN there)
 // and keeping NaN. This file is compiled with NaN semantics honoured (the rest of the library

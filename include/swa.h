@@ -156,8 +156,8 @@ int ve_gate_v_bwd(const void* x, int ldx, const float* Wg, const float* gate,
 
 /*
  * swa_doc_bounds — document segments of packed rows ("从4万美元到73美元" §6.1: BOS-aligned rows
- *   hold several documents; per-document attention is the variable-length attention its list of
- *   tried ideas names). A document is a maximal run of equal ids along a row; for each token
+ *   hold several documents; per-document attention is the variable-length attention that §7 of
+ *   the same page, "避坑指南", lists among the ideas tried). A document is a maximal run of equal ids along a row; for each token
  *   the call writes doc_bounds[(b*T + t)*2 + 0] = first position of its run and [... + 1] = one
  *   past the last. Computed once per batch; every attention call of the step can reuse it.
  *   doc_id: device (B,T) int32, read.   doc_bounds: device (B,T,2) int32, written.
@@ -266,8 +266,9 @@ int swa_bwd_dq_rowterms(const void* q, const void* k, const void* v, const void*
  */
 
 /*
- * fp8 forward variant ("从4万美元到73美元", intelliparadigm.com, the paragraph on mixed
- * precision: fp8 doubles matrix throughput over bf16 and needs scales to stay accurate).
+ * fp8 forward variant ("NanoGPT Speedrun：大模型训练效率的极限竞速指南", kongchang.com, section
+ * "工程与硬件优化", its paragraph on bf16 and fp8: fp8 can double matrix throughput over bf16
+ * and needs finer calibration (scales) to stay accurate).
  * Format: OCP e4m3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, no
  * infinities, largest finite 448, S.1111.111 = NaN), the format gfx950's fp8 MFMA reads.
  * Calibration: one float32 scale per tensor, x ~= scale * e4m3 value.

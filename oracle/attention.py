@@ -18,8 +18,8 @@ Passages followed:
   ``attention_fwd_online`` follows that recurrence block by block; it is a
   second statement of the forward used to pin the dense one.
 * Document masking (optional ``doc_id``): "从4万美元到73美元" §6.1 packs several
-  documents into one BOS-aligned row, and lists variable-length (per-document)
-  attention among the alternatives tried; "神级项目训练GPT-2仅需5分钟" notes that
+  documents into one BOS-aligned row, and §7 of that page ("避坑指南") lists
+  variable-length (per-document) attention among the alternatives tried; "神级项目训练GPT-2仅需5分钟" notes that
   longer rows with FlexAttention split fewer documents. Reading: a token attends
   only inside its own document, a document being a maximal run of equal
   ``doc_id`` values along the row; the causal window applies as well.

@@ -4,9 +4,9 @@ TEST INFRASTRUCTURE (see the package docstring).
 
 Passages followed:
 
-* "从4万美元到73美元" (intelliparadigm.com), the paragraph on mixed precision: fp8 is an
-  8-bit floating-point format that can double matrix throughput over bf16 but needs careful
-  calibration (scales) to stay accurate. The pages fix no fp8 encoding; reading: the OCP
+* "NanoGPT Speedrun：大模型训练效率的极限竞速指南" (kongchang.com), section "工程与硬件优化",
+  its paragraph on bf16 and fp8: fp8 is an 8-bit floating-point format that can double
+  matrix throughput over bf16 but needs finer calibration (scales) to stay accurate. The pages fix no fp8 encoding; reading: the OCP
   E4M3 format that gfx950's fp8 matrix instructions read (1 sign, 4 exponent bits with bias
   7, 3 mantissa bits; subnormals; no infinities; S.1111.111 is NaN; largest finite 448).
 * Reading (calibration): each of q_hat, k_hat, v is stored as e4m3 codes of x / s with one
