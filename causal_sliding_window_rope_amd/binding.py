@@ -39,6 +39,8 @@ SIGNATURES = {
     "swa_bwd_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "swa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
                      _I, _I, _I, _I, _I, _F, _I, _P]),
+    "swa_bwd_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                             _I, _I, _I, _I, _I, _F, _I, _P]),
     "swa_bwd_preprocess": (_I, [_P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _P]),
     "swa_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _S,
                           _I, _I, _I, _I, _I, _F, _I, _P]),
@@ -291,6 +293,26 @@ def swa_bwd(q, k, v, o, lse, dO, window: int, scale: float | None = None, ve=Non
           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dve), _ptr(dgate), _ptr(workspace),
           workspace.numel() * workspace.element_size(), B, T, H, D, int(window), float(scale),
           _dt(q), _stream())
+    if ve is not None:
+        return dq, dk, dv, dve, dgate
+    return dq, dk, dv
+
+
+def swa_bwd_noalloc(q, k, v, o, lse, dO, window: int, scale: float | None = None, ve=None,
+                    gate=None, grads=None, doc_bounds=None, ve_ids=None):
+    """swa_bwd on the library's static scratch instead of a workspace (same results)."""
+    B, T, H, D = q.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dO, "dO")):
+        _check(t, n, (B, T, H, D), q.dtype)
+    _check(lse, "lse", (B, H, T), torch.float32)
+    ids, rows = _ve_table(ve, gate, ve_ids, B, T, H, D, q.dtype)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    dq, dk, dv, dve, dgate = _grads(q, ve, ve_ids, B, T, H) if grads is None else grads
+    if doc_bounds is not None:
+        _check(doc_bounds, "doc_bounds", (B, T, 2), torch.int32)
+    _call("swa_bwd_noalloc", _ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), ids, rows,
+          _ptr(doc_bounds), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dve),
+          _ptr(dgate), B, T, H, D, int(window), float(scale), _dt(q), _stream())
     if ve is not None:
         return dq, dk, dv, dve, dgate
     return dq, dk, dv

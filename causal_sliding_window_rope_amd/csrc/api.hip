@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/swa.h"
@@ -254,12 +255,13 @@ size_t swa_bwd_workspace_size(int B, int T, int H, int D, swa_dtype dtype) {
   return swa::bwd_workspace_bytes(B, T, H, D, dtype == SWA_BF16);
 }
 
-static int check_bwd(const char* fn, const void* q, const void* k, const void* v, const void* ve,
-                     const float* gate, const int* ve_ids, int ve_rows, const int* doc_bounds,
-                     const void* o, const float* lse, const void* dO,
-                     const void* dq, const void* dk, const void* dv, const void* dve,
-                     const float* dgate, const void* workspace, size_t ws_bytes, int B, int T,
-                     int H, int D, int window, float scale, swa_dtype dtype, swa::AttnShape* a) {
+// Every argument of a backward call except the workspace.
+static int check_bwd_args(const char* fn, const void* q, const void* k, const void* v,
+                          const void* ve, const float* gate, const int* ve_ids, int ve_rows,
+                          const int* doc_bounds, const void* o, const float* lse, const void* dO,
+                          const void* dq, const void* dk, const void* dv, const void* dve,
+                          const float* dgate, int B, int T, int H, int D, int window, float scale,
+                          swa_dtype dtype, swa::AttnShape* a) {
   SWA_TRY(check_shape(fn, B, T, H, D, dtype));
   SWA_TRY(need(fn, "q", q)); SWA_TRY(need(fn, "k", k)); SWA_TRY(need(fn, "v", v));
   if (o) SWA_TRY(need(fn, "o", o));
@@ -275,7 +277,17 @@ static int check_bwd(const char* fn, const void* q, const void* k, const void* v
   *a = swa::AttnShape{B, T, H, D, 0, scale};
   a->bounds = doc_bounds;
   SWA_TRY(check_ve_table(fn, ve, ve_ids, ve_rows, H, D, a));
-  SWA_TRY(check_window_scale(fn, window, scale, T, &a->window));
+  return check_window_scale(fn, window, scale, T, &a->window);
+}
+
+static int check_bwd(const char* fn, const void* q, const void* k, const void* v, const void* ve,
+                     const float* gate, const int* ve_ids, int ve_rows, const int* doc_bounds,
+                     const void* o, const float* lse, const void* dO,
+                     const void* dq, const void* dk, const void* dv, const void* dve,
+                     const float* dgate, const void* workspace, size_t ws_bytes, int B, int T,
+                     int H, int D, int window, float scale, swa_dtype dtype, swa::AttnShape* a) {
+  SWA_TRY(check_bwd_args(fn, q, k, v, ve, gate, ve_ids, ve_rows, doc_bounds, o, lse, dO, dq, dk,
+                         dv, dve, dgate, B, T, H, D, window, scale, dtype, a));
   return check_ws(fn, workspace, ws_bytes, B, T, H, D, dtype);
 }
 
@@ -498,6 +510,74 @@ int swa_decode(const void* qn, const void* k_cache, const void* v_cache, const i
     return fail(SWA_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
   return hip_status(swa::launch_decode(qn, k_cache, v_cache, pos, o, lse, workspace, B, H, D, cap,
                                        w, scale, dtype == SWA_BF16, (hipStream_t)stream), fn);
+}
+
+// ---------------------------------------------------------------------------------------------
+// swa_bwd_noalloc: the backward on a scratch area inside the library's code object instead of a
+// caller workspace, for callers that cannot allocate device memory. The area is a static device
+// array, so each GPU the library runs on holds its own copy at its own address, resolved once
+// per device with hipGetSymbolAddress and cached; host code never uses the array's name as an
+// address (on the host it names a stand-in, not device memory). Nothing in it has to start at
+// zero: every row term the kernels read is written earlier in the same call (the rows, then the
+// zeroed slack behind them).
+// ---------------------------------------------------------------------------------------------
+}  // extern "C"
+
+static __device__ __align__(256) unsigned char scratch[SWA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];
+
+// Device address of `scratch` on the current device (resolved on the first call per device).
+int scratch_on_current_device(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SWA_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(SWA_ERR_UNSUPPORTED, "%s: device %d beyond the %d devices the scratch table holds",
+                fn, dev, kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(SWA_ERR_HIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn, dev,
+                  e != hipSuccess ? hipGetErrorString(e) : "null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return 0;
+}
+}  // namespace
+
+extern "C" {
+
+int swa_bwd_noalloc(const void* q, const void* k, const void* v, const void* ve,
+                    const float* gate, const int* ve_ids, int ve_rows, const int* doc_bounds,
+                    const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                    void* dve, float* dgate, int B, int T, int H, int D, int window, float scale,
+                    swa_dtype dtype, void* stream) {
+  const char* fn = "swa_bwd_noalloc";
+  swa::AttnShape a;
+  SWA_TRY(need(fn, "o", o));
+  SWA_TRY(check_bwd_args(fn, q, k, v, ve, gate, ve_ids, ve_rows, doc_bounds, o, lse, dO, dq, dk,
+                         dv, dve, dgate, B, T, H, D, window, scale, dtype, &a));
+  const bool bf = dtype == SWA_BF16;
+  const size_t need_ws = swa::bwd_workspace_bytes(B, T, H, D, bf);
+  if (need_ws > (size_t)SWA_NOALLOC_SCRATCH_BYTES)
+    return fail(SWA_ERR_WORKSPACE,
+                "%s: B*H*T = %lld rows need %zu bytes of scratch, more than the %zu bytes the "
+                "library holds (SWA_NOALLOC_SCRATCH_BYTES); call swa_bwd with a workspace",
+                fn, (long long)B * H * T, need_ws, (size_t)SWA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  SWA_TRY(scratch_on_current_device(fn, &ws));
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e = swa::launch_bwd_dq_rowterms(a, q, k, v, ve, gate, o, lse, dO, dq, ws, bf, s);
+  if (e == hipSuccess)
+    e = swa::launch_bwd_dkdv(a, q, k, v, ve, gate, lse, dO, dk, dv, dve, dgate, ws, bf, s);
+  return hip_status(e, fn);
 }
 
 }  // extern "C"

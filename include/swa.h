@@ -210,6 +210,28 @@ int swa_bwd(const void* q, const void* k, const void* v, const void* ve, const f
             size_t ws_bytes, int B, int T, int H, int D, int window, float scale, swa_dtype dtype,
             void* stream);
 
+/* Bytes of device scratch that swa_bwd_noalloc holds per GPU (its largest workspace). */
+#define SWA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * swa_bwd_noalloc — swa_bwd for callers that cannot allocate device memory: code being captured
+ *   into a HIP graph, tight serving loops, harnesses that forbid allocation. Same arguments,
+ *   kernels and results as swa_bwd (bitwise), without workspace and ws_bytes: the row terms go
+ *   to a static device array inside the library (SWA_NOALLOC_SCRATCH_BYTES per GPU, held until
+ *   the process ends), so B*H*T is limited to the sizes whose swa_bwd_workspace_size() fits it
+ *   (B*H*T <= 2,097,024 rows); larger sizes return SWA_ERR_WORKSPACE before anything is
+ *   enqueued. The call allocates nothing; its first call on a device resolves the array's
+ *   address there (hipGetSymbolAddress) with that device current, so call it with the
+ *   stream's device current. Every call on one GPU shares that GPU's array: calls that can
+ *   overlap on one GPU (other streams, other host threads) race and must be ordered by the
+ *   caller; calls in order on one stream are safe. Nothing in the array needs to start at zero.
+ */
+int swa_bwd_noalloc(const void* q, const void* k, const void* v, const void* ve,
+                    const float* gate, const int* ve_ids, int ve_rows, const int* doc_bounds,
+                    const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                    void* dve, float* dgate, int B, int T, int H, int D, int window, float scale,
+                    swa_dtype dtype, void* stream);
+
 /*
  * The stages of the backward, for callers that schedule or time them separately. Both orders
  * give the same results up to the rounding of delta (the one-call swa_bwd runs the first):

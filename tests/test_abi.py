@@ -156,6 +156,23 @@ def test_swa_bwd_validation(lib):
     assert dq(ve=P, gate=P, ids=P, rows=0) == INVALID   # table mode without rows
 
 
+def test_swa_bwd_noalloc_validation(lib):
+    """Checks that run on the host before the scratch is touched: bad arguments, and sizes whose
+    workspace would not fit the library's static scratch."""
+    def call(B=1, T=64, H=2, D=64, W=16, dq=P, o=P):
+        return lib.swa_bwd_noalloc(P, P, P, None, None, None, 0, None, o, P, P, dq, P, P, None,
+                                   None, B, T, H, D, W, 0.125, 1, None)
+
+    assert call(dq=None) == INVALID and call(o=None) == INVALID
+    assert call(W=0) == INVALID and call(D=96) == UNSUPPORTED
+    assert call(dq=MIS) == ALIGN
+    rows = 2_097_024                 # the most rows whose workspace fits 16 MiB
+    assert lib.swa_bwd_workspace_size(1, rows, 1, 64, 1) <= 16 << 20
+    assert lib.swa_bwd_workspace_size(1, rows + 1, 1, 64, 1) > 16 << 20
+    assert call(B=1, T=4096, H=1024) == WORKSPACE
+    assert b"SWA_NOALLOC_SCRATCH_BYTES" in lib.swa_last_error()
+
+
 def test_fp8_validation(lib):
     assert lib.swa_fp8_v_bytes(2, 100, 3, 128) == 2 * 3 * 128 * 128     # T padded to 128
     assert lib.swa_fp8_v_bytes(2, 100, 3, 96) == 0
