@@ -140,8 +140,11 @@ def run_bench(args):
         g["dve"] = torch.empty((B, T, H * D), dtype=torch.bfloat16, device="cuda")
         g["dgate"] = torch.empty((B, T, H), dtype=torch.float32, device="cuda")
         g["dWg"] = torch.empty((32, H), dtype=torch.float32, device="cuda")
-    ws = torch.empty(sw.swa_bwd_workspace_size(B, T, H, D, torch.bfloat16), dtype=torch.uint8,
-                     device="cuda")
+    stored_ds = args.bwd == "ds"
+    # one workspace serves every layer (sized for the widest window)
+    ws_bytes = (sw.swa_bwd_ds_workspace_size(B, T, H, D, max(cfg["windows"]), torch.bfloat16)
+                if stored_ds else sw.swa_bwd_workspace_size(B, T, H, D, torch.bfloat16))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     if cfg["gate"]:
         g["gws"] = torch.empty(sw.load().ve_gate_v_bwd_workspace_size(B, T, H), dtype=torch.uint8,
                                device="cuda")
@@ -192,17 +195,33 @@ def run_bench(args):
                 fids, frows = ids, rows
             elif cfg["gate"]:
                 v = t["veff"]
-            # dQ first: its kernel also writes the row terms (delta, lse) that dK/dV reads
-            if rec: rec["bwd"][li][0].record()
-            call("swa_bwd_dq_rowterms", P(t["qn"]), P(t["kn"]), P(v), P(ve), P(gate), P(fids),
-                 frows, P(bounds), P(t["o"]), P(t["lse"]), P(t["dO"]), P(g["dqn"]), P(ws), nws,
-                 B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
-            if rec: rec["bwd"][li][1].record()
-            call("swa_bwd_dkdv", P(t["qn"]), P(t["kn"]), P(v), P(ve), P(gate), P(fids), frows,
-                 P(bounds), P(t["lse"]),
-                 P(t["dO"]), P(g["dkn"]), P(g["dv"]), P(dve), P(dgate), P(ws), nws,
-                 B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
-            if rec: rec["bwd"][li][2].record()
+            if stored_ds:
+                # row terms (delta, lse), then dK/dV storing the bf16 dS it forms, then dQ from
+                # the stored dS
+                if rec: rec["bwd"][li][0].record()
+                call("swa_bwd_preprocess", P(t["o"]), P(t["dO"]), P(t["lse"]), P(ws), nws,
+                     B, T, H, D, sw.SWA_BF16, stream)
+                if rec: rec["bwd"][li][1].record()
+                call("swa_bwd_dkdv_ds", P(t["qn"]), P(t["kn"]), P(v), P(ve), P(gate), P(fids),
+                     frows, P(bounds), P(t["lse"]), P(t["dO"]), P(g["dkn"]), P(g["dv"]), P(dve),
+                     P(dgate), P(ws), nws, B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
+                if rec: rec["bwd"][li][2].record()
+                call("swa_bwd_dq_ds", P(t["kn"]), P(bounds), P(g["dqn"]), P(ws), nws,
+                     B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
+                if rec: rec["bwd"][li][3].record()
+            else:
+                # dQ first: its kernel also writes the row terms (delta, lse) that dK/dV reads
+                if rec: rec["bwd"][li][0].record()
+                if rec: rec["bwd"][li][1].record()
+                call("swa_bwd_dq_rowterms", P(t["qn"]), P(t["kn"]), P(v), P(ve), P(gate), P(fids),
+                     frows, P(bounds), P(t["o"]), P(t["lse"]), P(t["dO"]), P(g["dqn"]), P(ws),
+                     nws, B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
+                if rec: rec["bwd"][li][2].record()
+                call("swa_bwd_dkdv", P(t["qn"]), P(t["kn"]), P(v), P(ve), P(gate), P(fids), frows,
+                     P(bounds), P(t["lse"]),
+                     P(t["dO"]), P(g["dkn"]), P(g["dv"]), P(dve), P(dgate), P(ws), nws,
+                     B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
+                if rec: rec["bwd"][li][3].record()
             call("rope_qknorm_bwd", P(t["q"]), P(t["k"]), P(cs), P(g["dqn"]), P(g["dkn"]), P(g["dq"]),
                  P(g["dk"]), B, T, H, D, 1e-6, sw.SWA_BF16, stream)
             if cfg["gate"]:
@@ -217,7 +236,7 @@ def run_bench(args):
         step(None)
     torch.cuda.synchronize()
     nl = len(layers)
-    recs = [{"fwd": [[ev(), ev()] for _ in range(nl)], "bwd": [[ev() for _ in range(3)] for _ in range(nl)]}
+    recs = [{"fwd": [[ev(), ev()] for _ in range(nl)], "bwd": [[ev() for _ in range(4)] for _ in range(nl)]}
             for _ in range(args.steps)]
     e0, e1 = ev(), ev()
     torch.cuda.synchronize()          # one GPU: no process group, so no barrier is needed
@@ -255,8 +274,12 @@ def run_bench(args):
         step_ms = e0.elapsed_time(e1) / args.steps
 
     fwd_ms = sum(r["fwd"][l][0].elapsed_time(r["fwd"][l][1]) for r in recs for l in range(nl))
-    dq_ms = sum(r["bwd"][l][0].elapsed_time(r["bwd"][l][1]) for r in recs for l in range(nl))
-    kv_ms = sum(r["bwd"][l][1].elapsed_time(r["bwd"][l][2]) for r in recs for l in range(nl))
+    seg = lambda a, b: sum(r["bwd"][l][a].elapsed_time(r["bwd"][l][b]) for r in recs
+                           for l in range(nl))
+    if stored_ds:   # events: | preprocess | dK/dV (+ dS store) | dQ from dS |
+        pre_ms, kv_ms, dq_ms = seg(0, 1), seg(1, 2), seg(2, 3)
+    else:           # events: | | dQ with the row terms | dK/dV |
+        pre_ms, dq_ms, kv_ms = seg(0, 1), seg(1, 2), seg(2, 3)
     launches = args.steps * nl
 
     npairs = sum(visible_pairs(cfg, W, starts) for W in cfg["windows"]) * H
@@ -264,19 +287,21 @@ def run_bench(args):
     bwd_flop = 10 * D * npairs
     flop = fwd_flop + bwd_flop
     value = flop / (step_ms * 1e-3) / 1e12
-    core_ms = (fwd_ms + kv_ms + dq_ms) / args.steps
+    core_ms = (fwd_ms + pre_ms + kv_ms + dq_ms) / args.steps
     fwd_tf = fwd_flop / (fwd_ms / args.steps * 1e-3) / 1e12
-    bwd_tf = bwd_flop / ((kv_ms + dq_ms) / args.steps * 1e-3) / 1e12
-    # algorithmic FLOPs of each backward kernel: dK/dV kernel recomputes S and dP and forms dV,
-    # dK (8*D per pair); the dQ kernel recomputes S and dP and forms dQ (6*D per pair). The
-    # metric credits 10*D per pair to the backward as a whole.
+    bwd_tf = bwd_flop / ((pre_ms + kv_ms + dq_ms) / args.steps * 1e-3) / 1e12
+    # algorithmic FLOPs of each backward kernel: the dK/dV kernel recomputes S and dP and forms
+    # dV, dK (8*D per pair); the dQ kernel forms dQ from the stored dS (2*D per pair), or, on the
+    # recomputing path, recomputes S and dP once more (6*D per pair). The metric credits 10*D
+    # per pair to the backward as a whole.
     kv_flop = 8 * D * npairs
-    dq_flop = 6 * D * npairs
+    dq_flop = (2 if stored_ds else 6) * D * npairs
 
     # dominant kernel: the one with the largest share of the step
-    cands = [("dkdv_bf16_kernel (swa_bwd_dkdv)", kv_ms, kv_flop),
-             ("fwd_bf16_kernel (swa_fwd)", fwd_ms, fwd_flop),
-             ("dq_bf16_kernel (swa_bwd_dq_rowterms)", dq_ms, dq_flop)]
+    kv_name = "dkdv_bf16_kernel (swa_bwd_dkdv_ds)" if stored_ds else "dkdv_bf16_kernel (swa_bwd_dkdv)"
+    dq_name = "dq_ds_kernel (swa_bwd_dq_ds)" if stored_ds else "dq_bf16_kernel (swa_bwd_dq_rowterms)"
+    cands = [(kv_name, kv_ms, kv_flop), ("fwd_bf16_kernel (swa_fwd)", fwd_ms, fwd_flop),
+             (dq_name, dq_ms, dq_flop)]
     dom, dom_total_ms, dom_total_flop = max(cands, key=lambda x: x[1])
     dom_ms, dom_flop = dom_total_ms / launches, dom_total_flop / nl
     achieved = dom_flop / (dom_ms * 1e-3) / 1e12
@@ -304,9 +329,12 @@ def run_bench(args):
             "prologue_and_gate_ms_per_step": round(eager_ms - core_ms, 4),
             "swa_fwd_tflops": round(fwd_tf, 2),
             "swa_bwd_tflops_credited": round(bwd_tf, 2),
+            "backward": ("row terms, dK/dV storing dS, dQ from the stored dS" if stored_ds
+                         else "dQ with the row terms, then dK/dV (S and dP recomputed twice)"),
             "swa_bwd_dkdv_tflops_executed": round(kv_flop / (kv_ms / args.steps * 1e-3) / 1e12, 2),
             "swa_bwd_dq_tflops_executed": round(dq_flop / (dq_ms / args.steps * 1e-3) / 1e12, 2),
             "swa_fwd_ms_per_step": round(fwd_ms / args.steps, 4),
+            "swa_bwd_preprocess_ms_per_step": round(pre_ms / args.steps, 4),
             "swa_bwd_dkdv_ms_per_step": round(kv_ms / args.steps, 4),
             "swa_bwd_dq_ms_per_step": round(dq_ms / args.steps, 4),
             "wall_s_timed_region": round(wall, 3),
@@ -322,8 +350,9 @@ def run_bench(args):
 # committed counter figures for that kernel)
 KERNEL_SOURCES = {
     "fwd_bf16_kernel": ("fwd.hip", "common.h"),
-    "dkdv_bf16_kernel": ("bwd.hip", "common.h"),
+    "dkdv_bf16_kernel": ("bwd.hip", "common.h", "dsbuf.h"),
     "dq_bf16_kernel": ("dq.hip", "common.h"),
+    "dq_ds_kernel": ("dqds.hip", "common.h", "dsbuf.h"),
 }
 
 
@@ -681,6 +710,9 @@ def main():
                          "one captured HIP graph (replays) instead of eager launches; the "
                          "per-kernel figures still come from an eager pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bwd", choices=("ds", "recompute"), default="ds",
+                    help="backward: dS stored by the dK/dV kernel and read by the dQ kernel "
+                         "(default), or S and dP recomputed in both")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="only run a plain device-to-device copy of this many MiB 5 times (used to "
                          "scale HBM byte counters under rocprofv3), then exit")

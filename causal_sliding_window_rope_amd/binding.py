@@ -39,6 +39,12 @@ SIGNATURES = {
     "swa_bwd_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "swa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
                      _I, _I, _I, _I, _I, _F, _I, _P]),
+    "swa_bwd_ds_workspace_size": (_S, [_I, _I, _I, _I, _I, _I]),
+    "swa_bwd_ds": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
+                        _I, _I, _I, _I, _I, _F, _I, _P]),
+    "swa_bwd_dkdv_ds": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _S,
+                             _I, _I, _I, _I, _I, _F, _I, _P]),
+    "swa_bwd_dq_ds": (_I, [_P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _F, _I, _P]),
     "swa_bwd_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                              _I, _I, _I, _I, _I, _F, _I, _P]),
     "swa_bwd_preprocess": (_I, [_P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _P]),
@@ -293,6 +299,47 @@ def swa_bwd(q, k, v, o, lse, dO, window: int, scale: float | None = None, ve=Non
           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dve), _ptr(dgate), _ptr(workspace),
           workspace.numel() * workspace.element_size(), B, T, H, D, int(window), float(scale),
           _dt(q), _stream())
+    if ve is not None:
+        return dq, dk, dv, dve, dgate
+    return dq, dk, dv
+
+
+def swa_bwd_ds_workspace_size(B: int, T: int, H: int, D: int, window: int,
+                              dtype: torch.dtype) -> int:
+    return load().swa_bwd_ds_workspace_size(B, T, H, D, int(window),
+                                            SWA_BF16 if dtype == torch.bfloat16 else SWA_F32)
+
+
+def swa_bwd_ds(q, k, v, o, lse, dO, window: int, scale: float | None = None, ve=None, gate=None,
+               workspace=None, grads=None, doc_bounds=None, ve_ids=None, stages: bool = False):
+    """The backward with the score gradient stored (swa_bwd_ds), or with stages=True its C-ABI
+    stages (preprocess, dK/dV storing dS, dq from dS). Returns as swa_bwd."""
+    B, T, H, D = q.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dO, "dO")):
+        _check(t, n, (B, T, H, D), q.dtype)
+    _check(lse, "lse", (B, H, T), torch.float32)
+    ids, rows = _ve_table(ve, gate, ve_ids, B, T, H, D, q.dtype)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if workspace is None:
+        workspace = torch.empty(swa_bwd_ds_workspace_size(B, T, H, D, window, q.dtype),
+                                dtype=torch.uint8, device=q.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    dq, dk, dv, dve, dgate = _grads(q, ve, ve_ids, B, T, H) if grads is None else grads
+    if doc_bounds is not None:
+        _check(doc_bounds, "doc_bounds", (B, T, 2), torch.int32)
+    st, dt = _stream(), _dt(q)
+    common = (_ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate), ids, rows, _ptr(doc_bounds))
+    if not stages:
+        _call("swa_bwd_ds", *common, _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv),
+              _ptr(dve), _ptr(dgate), _ptr(workspace), nbytes, B, T, H, D, int(window),
+              float(scale), dt, st)
+    else:
+        _call("swa_bwd_preprocess", _ptr(o), _ptr(dO), _ptr(lse), _ptr(workspace), nbytes, B, T,
+              H, D, dt, st)
+        _call("swa_bwd_dkdv_ds", *common, _ptr(lse), _ptr(dO), _ptr(dk), _ptr(dv), _ptr(dve),
+              _ptr(dgate), _ptr(workspace), nbytes, B, T, H, D, int(window), float(scale), dt, st)
+        _call("swa_bwd_dq_ds", _ptr(k), _ptr(doc_bounds), _ptr(dq), _ptr(workspace), nbytes, B, T,
+              H, D, int(window), float(scale), dt, st)
     if ve is not None:
         return dq, dk, dv, dve, dgate
     return dq, dk, dv

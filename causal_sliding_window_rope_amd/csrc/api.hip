@@ -84,6 +84,31 @@ int check_ws(const char* fn, const void* workspace, size_t ws_bytes, int B, int 
   return 0;
 }
 
+// Workspace of the stored-dS backward: the row terms, then (bf16) the dS^T chunks at the next
+// 256-byte boundary. W is the clamped window (1..T).
+size_t ds_ws_rowterm_bytes(int B, int T, int H, int D, int dtype) {
+  return (swa::bwd_workspace_bytes(B, T, H, D, dtype == SWA_BF16) + 255) & ~(size_t)255;
+}
+size_t ds_ws_bytes(int B, int T, int H, int D, int W, int dtype) {
+  const size_t rt = ds_ws_rowterm_bytes(B, T, H, D, dtype);
+  return dtype == SWA_BF16 ? rt + swa::ds_buffer_bytes(B, T, H, W) : rt;
+}
+
+int check_ws_ds(const char* fn, const void* workspace, size_t ws_bytes, int B, int T, int H, int D,
+                int W, int dtype) {
+  const size_t need_ws = ds_ws_bytes(B, T, H, D, W, dtype);
+  if (!workspace || ws_bytes < need_ws)
+    return fail(SWA_ERR_WORKSPACE, "%s: workspace of %zu bytes required (got %zu; see "
+                "swa_bwd_ds_workspace_size)", fn, need_ws, workspace ? ws_bytes : (size_t)0);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(SWA_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+  return 0;
+}
+
+void* ds_part(void* workspace, int B, int T, int H, int D, int dtype) {
+  return static_cast<char*>(workspace) + ds_ws_rowterm_bytes(B, T, H, D, dtype);
+}
+
 }  // namespace
 
 #define SWA_TRY(expr)        \
@@ -308,6 +333,78 @@ int swa_bwd(const void* q, const void* k, const void* v, const void* ve, const f
   if (e == hipSuccess)
     e = swa::launch_bwd_dkdv(a, q, k, v, ve, gate, lse, dO, dk, dv, dve, dgate, workspace, bf, s);
   return hip_status(e, fn);
+}
+
+size_t swa_bwd_ds_workspace_size(int B, int T, int H, int D, int window, swa_dtype dtype) {
+  if (B < 1 || T < 1 || H < 1 || (D != 64 && D != 128)) return 0;
+  if (window == 0 || window < SWA_WINDOW_FULL) return 0;
+  const int W = (window == SWA_WINDOW_FULL || window > T) ? T : window;
+  return ds_ws_bytes(B, T, H, D, W, dtype);
+}
+
+int swa_bwd_ds(const void* q, const void* k, const void* v, const void* ve, const float* gate,
+               const int* ve_ids, int ve_rows, const int* doc_bounds, const void* o,
+               const float* lse, const void* dO, void* dq, void* dk, void* dv, void* dve,
+               float* dgate, void* workspace, size_t ws_bytes, int B, int T, int H, int D,
+               int window, float scale, swa_dtype dtype, void* stream) {
+  const char* fn = "swa_bwd_ds";
+  swa::AttnShape a;
+  SWA_TRY(need(fn, "o", o));
+  SWA_TRY(check_bwd_args(fn, q, k, v, ve, gate, ve_ids, ve_rows, doc_bounds, o, lse, dO, dq, dk,
+                         dv, dve, dgate, B, T, H, D, window, scale, dtype, &a));
+  SWA_TRY(check_ws_ds(fn, workspace, ws_bytes, B, T, H, D, a.window, dtype));
+  const bool bf = dtype == SWA_BF16;
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (!bf) {
+    // float32: the recomputing kernels (no dS is stored)
+    e = swa::launch_bwd_dq_rowterms(a, q, k, v, ve, gate, o, lse, dO, dq, workspace, bf, s);
+    if (e == hipSuccess)
+      e = swa::launch_bwd_dkdv(a, q, k, v, ve, gate, lse, dO, dk, dv, dve, dgate, workspace, bf, s);
+    return hip_status(e, fn);
+  }
+  void* ds = ds_part(workspace, B, T, H, D, dtype);
+  e = swa::launch_bwd_pre(a, o, dO, lse, workspace, bf, s);
+  if (e == hipSuccess)
+    e = swa::launch_bwd_dkdv(a, q, k, v, ve, gate, lse, dO, dk, dv, dve, dgate, workspace, bf, s,
+                             ds);
+  if (e == hipSuccess) e = swa::launch_dq_from_ds(a, k, ds, dq, s);
+  return hip_status(e, fn);
+}
+
+int swa_bwd_dkdv_ds(const void* q, const void* k, const void* v, const void* ve,
+                    const float* gate, const int* ve_ids, int ve_rows, const int* doc_bounds,
+                    const float* lse, const void* dO, void* dk, void* dv, void* dve, float* dgate,
+                    void* workspace, size_t ws_bytes, int B, int T, int H, int D, int window,
+                    float scale, swa_dtype dtype, void* stream) {
+  const char* fn = "swa_bwd_dkdv_ds";
+  swa::AttnShape a;
+  if (dtype != SWA_BF16)
+    return fail(SWA_ERR_UNSUPPORTED, "%s: the stored-dS stages are bfloat16 only", fn);
+  // dq is not used by this stage; dk stands in for it in the shared checks
+  SWA_TRY(check_bwd_args(fn, q, k, v, ve, gate, ve_ids, ve_rows, doc_bounds, nullptr, lse, dO, dk,
+                         dk, dv, dve, dgate, B, T, H, D, window, scale, dtype, &a));
+  SWA_TRY(check_ws_ds(fn, workspace, ws_bytes, B, T, H, D, a.window, dtype));
+  return hip_status(swa::launch_bwd_dkdv(a, q, k, v, ve, gate, lse, dO, dk, dv, dve, dgate,
+                                         workspace, true, (hipStream_t)stream,
+                                         ds_part(workspace, B, T, H, D, dtype)), fn);
+}
+
+int swa_bwd_dq_ds(const void* k, const int* doc_bounds, void* dq, void* workspace,
+                  size_t ws_bytes, int B, int T, int H, int D, int window, float scale,
+                  swa_dtype dtype, void* stream) {
+  const char* fn = "swa_bwd_dq_ds";
+  if (dtype != SWA_BF16)
+    return fail(SWA_ERR_UNSUPPORTED, "%s: the stored-dS stages are bfloat16 only", fn);
+  SWA_TRY(check_shape(fn, B, T, H, D, dtype));
+  SWA_TRY(need(fn, "k", k)); SWA_TRY(need(fn, "dq", dq));
+  SWA_TRY(opt(fn, "doc_bounds", doc_bounds));
+  swa::AttnShape a{B, T, H, D, 0, scale};
+  a.bounds = doc_bounds;
+  SWA_TRY(check_window_scale(fn, window, scale, T, &a.window));
+  SWA_TRY(check_ws_ds(fn, workspace, ws_bytes, B, T, H, D, a.window, dtype));
+  return hip_status(swa::launch_dq_from_ds(a, k, ds_part(workspace, B, T, H, D, dtype), dq,
+                                           (hipStream_t)stream), fn);
 }
 
 int swa_bwd_preprocess(const void* o, const void* dO, const float* lse, void* workspace,

@@ -22,59 +22,82 @@
 //  * Value-embedding gate: v_eff = v + gate * ve is formed in fp32 when the V rows are loaded;
 //    the epilogue writes dv = dv_eff, dve = gate * dv_eff and dgate = sum_d dv_eff * ve.
 #include "common.h"
+#include "dsbuf.h"
 #include "internal.h"
 
 namespace swa {
 
 // ------------------------------------------------------------------------------------------
 // ndelta_i = -sum_d dO[i, d] * O[i, d] and nlse2_i = -lse_i * log2(e), both (B, H, T).
+// One workgroup = 64 consecutive positions t of one (b, h): D / (16 / sizeof(E)) lanes per row
+// (one 16-byte load of O and of dO each), all the rows' loads issued before any arithmetic, and
+// the row terms written as contiguous runs of the (B, H, T) arrays.
 // ------------------------------------------------------------------------------------------
 // Rows of slack zeroed behind each row-term array (a query tile is 128 rows).
 constexpr int kRowTermSlackRows = 128;
+constexpr int kPreRows = 64;   // positions per workgroup
 
 template <typename E, int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(const E* __restrict__ o,
                                                       const E* __restrict__ dO,
                                                       const float* __restrict__ lse,
                                                       float* __restrict__ ndelta,
-                                                      float* __restrict__ nlse2, int rows, int T,
-                                                      int H) {
-  constexpr int VPT = 16 / sizeof(E), TPR = D / VPT;
-  const int lr = threadIdx.x % TPR;
-  const int row = blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
-  if (row >= rows) {
-    // The 128-query tiles of the bf16 dK/dV kernel read the row terms of the last head up to
-    // 127 rows past its end, in the slack behind each array: zero them, so that a workspace
-    // holding NaN or Inf bit patterns cannot reach dS = P (dP - delta) of a masked query.
-    if (row < rows + kRowTermSlackRows && lr == 0) { ndelta[row] = 0.f; nlse2[row] = 0.f; }
+                                                      float* __restrict__ nlse2, int T, int H,
+                                                      int nbh) {
+  constexpr int VPT = 16 / sizeof(E), TPR = D / VPT, RPP = 256 / TPR, PASSES = kPreRows / RPP;
+  const int bh = blockIdx.y, b = bh / H, h = bh - b * H;
+  const int t0 = blockIdx.x * kPreRows;
+  // The 128-query tiles of the bf16 dK/dV kernel read the row terms of the last head up to 127
+  // rows past its end, in the slack behind each array: positions T .. T + 127 of the last head
+  // are written as zeros, so that a workspace holding NaN or Inf bit patterns cannot reach
+  // dS = P (dP - delta) of a masked query.
+  auto zero_slack = [&](int t) {
+    if (bh == nbh - 1 && t >= T && t - T < kRowTermSlackRows) {
+      ndelta[(size_t)nbh * T + (t - T)] = 0.f;
+      nlse2[(size_t)nbh * T + (t - T)] = 0.f;
+    }
+  };
+  if (t0 >= T) {
+    if (threadIdx.x < kPreRows) zero_slack(t0 + (int)threadIdx.x);
     return;
   }
-  const size_t off = (size_t)row * D + lr * VPT;
-  const uint4 a = *reinterpret_cast<const uint4*>(o + off);
-  const uint4 g = *reinterpret_cast<const uint4*>(dO + off);
-  float acc;
-  if constexpr (VPT == 4) {
-    acc = __uint_as_float(a.x) * __uint_as_float(g.x);
-    acc = fmaf(__uint_as_float(a.y), __uint_as_float(g.y), acc);
-    acc = fmaf(__uint_as_float(a.z), __uint_as_float(g.z), acc);
-    acc = fmaf(__uint_as_float(a.w), __uint_as_float(g.w), acc);
-  } else {
-    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, gw[4] = {g.x, g.y, g.z, g.w};
-    acc = 0.f;
+  const int lr = threadIdx.x % TPR, rr = threadIdx.x / TPR;
+  uint4 a[PASSES], g[PASSES];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc = fmaf(bf_lo(aw[e]), bf_lo(gw[e]), acc);
-      acc = fmaf(bf_hi(aw[e]), bf_hi(gw[e]), acc);
-    }
+  for (int i = 0; i < PASSES; ++i) {
+    const int t = min(t0 + i * RPP + rr, T - 1);
+    const size_t off = (((size_t)b * T + t) * H + h) * D + lr * VPT;
+    a[i] = *reinterpret_cast<const uint4*>(o + off);
+    g[i] = *reinterpret_cast<const uint4*>(dO + off);
   }
 #pragma unroll
-  for (int m = 1; m < TPR; m <<= 1) acc += xor_shfl(acc, m);
-  if (lr == 0) {
-    const int h = row % H, t = (row / H) % T, b = row / (H * T);
-    const size_t r = ((size_t)b * H + h) * T + t;
-    // stored negated: the bf16 kernels seed their S and dP accumulators with these
-    ndelta[r] = -acc;
-    nlse2[r] = -lse[r] * kLog2e;   // log2-domain row term of the exp2
+  for (int i = 0; i < PASSES; ++i) {
+    float acc;
+    if constexpr (VPT == 4) {
+      acc = __uint_as_float(a[i].x) * __uint_as_float(g[i].x);
+      acc = fmaf(__uint_as_float(a[i].y), __uint_as_float(g[i].y), acc);
+      acc = fmaf(__uint_as_float(a[i].z), __uint_as_float(g[i].z), acc);
+      acc = fmaf(__uint_as_float(a[i].w), __uint_as_float(g[i].w), acc);
+    } else {
+      const uint32_t aw[4] = {a[i].x, a[i].y, a[i].z, a[i].w};
+      const uint32_t gw[4] = {g[i].x, g[i].y, g[i].z, g[i].w};
+      acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = fmaf(bf_lo(aw[e]), bf_lo(gw[e]), acc);
+        acc = fmaf(bf_hi(aw[e]), bf_hi(gw[e]), acc);
+      }
+    }
+    acc = group_sum<TPR>(acc);
+    const int t = t0 + i * RPP + rr;
+    if (lr == 0 && t < T) {
+      const size_t r = (size_t)bh * T + t;
+      // stored negated: the bf16 kernels seed their S and dP accumulators with these
+      ndelta[r] = -acc;
+      nlse2[r] = -lse[r] * kLog2e;   // log2-domain row term of the exp2
+    } else if (lr == 0) {
+      zero_slack(t);
+    }
   }
 }
 
@@ -99,6 +122,8 @@ struct Params {
   const int* ve_ids;   // table mode: ve is (ve_rows, H*D), dve_tab the float table gradient
   int ve_rows;
   float* dve_tab;
+  bf16* ds;      // stored dS^T (dsbuf.h), written by the STORE_DS instantiation
+  int nslot;     // query-tile slots per key block in ds
   int B, T, H, window, nkb;
   float c;       // scale * log2(e)
   float scale;
@@ -145,7 +170,7 @@ __device__ __forceinline__ void mfma_ds_interleave() {
   }
 }
 
-template <int D, bool GATE, bool DOC>
+template <int D, bool GATE, bool DOC, bool STORE_DS>
 __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dkdv_bf16_kernel(Params p) {
   using C = Cfg<D>;
   constexpr int NDB = D / 32, NKS = D / 16;
@@ -252,6 +277,28 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dkdv_bf16_kernel(Params 
   // number of queries (from the key itself on) that see this lane's key
   const unsigned mask_n = mykey < T ? (unsigned)(hi_key - mykey + 1) : 0u;
 
+  // Stored dS^T: resource at this head's chunks; each lane writes its 32 bytes of a chunk at
+  // 64 * key + 32 * hi (the chunk layout of dsbuf.h).
+  const __amdgpu_buffer_rsrc_t ds_rsrc =
+      buf_rsrc(STORE_DS ? reinterpret_cast<char*>(p.ds) + dsb::block_offset(bh, 0, 0, p.nkb, p.nslot)
+                        : nullptr);
+  const unsigned ds_voff = 64u * l32 + 32u * hi;
+  // A unit's dS^T is stored at the start of the next computed unit (the last one after the
+  // loop). The wait for a tile's copies at its end is a wait for every vector-memory operation
+  // of the wave, stores included (one counter; loads and stores may complete out of order), so
+  // stores issued in a tile's last unit would expose their write latency at every tile end;
+  // issued a unit later, they have completed by then.
+  u32x4 pend0 = {}, pend1 = {};
+  int pend_off = -1;   // chunk offset of the pending store, -1: none
+  auto store_pending = [&]() __attribute__((always_inline)) {
+    if constexpr (STORE_DS) {
+      if (pend_off >= 0) {
+        __builtin_amdgcn_raw_buffer_store_b128(pend0, ds_rsrc, ds_voff, pend_off, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(pend1, ds_rsrc, ds_voff + 16u, pend_off, 0);
+      }
+    }
+  };
+
   // One query tile: recompute S, P, dP, dS in 32-query halves; accumulate dV and dK.
   auto tile = [&](const lds_t<bf16>* Qs, const lds_t<bf16>* Os, const lds_t<float>* Ls,
                   const lds_t<float>* Dls, int qt) {
@@ -279,6 +326,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dkdv_bf16_kernel(Params 
       }
       const bool need_mask = (qm < kw + 31) || (qm + 31 > whi0) || (qm + 32 > T) ||
                              (kw + 32 > T);
+      store_pending();
       // The LDS operands of each phase are requested one phase ahead, so the reads overlap one
       // another and the MFMAs of the previous phase: the S operands (row term, Q) during the
       // previous unit's dK MFMAs, the dP operands (row term, dO) between the S MFMAs, the dV
@@ -375,6 +423,12 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dkdv_bf16_kernel(Params 
         sbf[a >> 1][e0] = d01[0]; sbf[a >> 1][e0 + 1] = d01[1];
         sbf[a >> 1][e0 + 2] = d23[0]; sbf[a >> 1][e0 + 3] = d23[1];
       }
+      if constexpr (STORE_DS) {
+        pend0 = __builtin_bit_cast(u32x4, sbf[0]);
+        pend1 = __builtin_bit_cast(u32x4, sbf[1]);
+        pend_off = (int)(dsb::block_offset(0, kbk, qt - kbk, p.nkb, p.nslot) +
+                         (size_t)((wave * 4 + mb) * dsb::CHUNK_BYTES));
+      }
       sched_fence();
       // dK += dS^T Q, with the next unit's S operands read between the MFMAs
 #pragma unroll
@@ -404,6 +458,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dkdv_bf16_kernel(Params 
     wait_vmem();
     lds_sync();
   }
+  store_pending();
 
   // Epilogue: lane owns d = 32 db + l32 of keys kw + 8(i/4) + 4 hi + (i%4).
 #pragma unroll
@@ -569,21 +624,21 @@ size_t bwd_workspace_bytes(int B, int T, int H, int D, bool bf16) {
 template <typename E, int D>
 static void launch_pre(const void* o, const void* dO, const float* lse, float* ndelta, float* nlse2,
                        int B, int T, int H, hipStream_t s) {
-  constexpr int TPR = D / (16 / sizeof(E));
-  const int rows = B * T * H;
-  const int rpb = 256 / TPR;
-  const int span = rows + kRowTermSlackRows;   // the rows, then the zeroed slack
-  hipLaunchKernelGGL((bwd_pre_kernel<E, D>), dim3((span + rpb - 1) / rpb), dim3(256), 0, s,
-                     (const E*)o, (const E*)dO, lse, ndelta, nlse2, rows, T, H);
+  // the positions of each head, then (last head only) the zeroed slack
+  const dim3 grid((T + kPreRows - 1) / kPreRows + kRowTermSlackRows / kPreRows, B * H);
+  hipLaunchKernelGGL((bwd_pre_kernel<E, D>), grid, dim3(256), 0, s, (const E*)o, (const E*)dO,
+                     lse, ndelta, nlse2, T, H, B * H);
 }
 
-template <int D, bool GATE>
+template <int D, bool GATE, bool STORE_DS>
 static hipError_t launch_dkdv_bf16_t(const AttnShape& a, const bwdk::Params& p, hipStream_t s) {
   const unsigned blocks = (unsigned)p.nkb * a.B * a.H;
   if (a.bounds)
-    hipLaunchKernelGGL((bwdk::dkdv_bf16_kernel<D, GATE, true>), dim3(blocks), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwdk::dkdv_bf16_kernel<D, GATE, true, STORE_DS>), dim3(blocks), dim3(256),
+                       0, s, p);
   else
-    hipLaunchKernelGGL((bwdk::dkdv_bf16_kernel<D, GATE, false>), dim3(blocks), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwdk::dkdv_bf16_kernel<D, GATE, false, STORE_DS>), dim3(blocks),
+                       dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -617,7 +672,7 @@ hipError_t launch_bwd_pre(const AttnShape& a, const void* o, const void* dO, con
 hipError_t launch_bwd_dkdv(const AttnShape& a, const void* q, const void* k, const void* v,
                            const void* ve, const float* gate, const float* lse, const void* dO,
                            void* dk, void* dv, void* dve, float* dgate, void* ws, bool is_bf16,
-                           hipStream_t s) {
+                           hipStream_t s, void* ds) {
   const int B = a.B, T = a.T, H = a.H, D = a.D;
   const WsView w = ws_view(ws, B, T, H);
   if (is_bf16) {
@@ -631,9 +686,17 @@ hipError_t launch_bwd_dkdv(const AttnShape& a, const void* q, const void* k, con
     p.nkb = (T + bwdk::BNK - 1) / bwdk::BNK;
     p.c = a.scale * kLog2e;
     p.scale = a.scale;
+    p.ds = (bf16*)ds;
+    p.nslot = dsb::nslot(T, a.window);
     const bool g = gate != nullptr;
-    if (D == 64) return g ? launch_dkdv_bf16_t<64, true>(a, p, s) : launch_dkdv_bf16_t<64, false>(a, p, s);
-    return g ? launch_dkdv_bf16_t<128, true>(a, p, s) : launch_dkdv_bf16_t<128, false>(a, p, s);
+    if (ds) {
+      if (D == 64)
+        return g ? launch_dkdv_bf16_t<64, true, true>(a, p, s) : launch_dkdv_bf16_t<64, false, true>(a, p, s);
+      return g ? launch_dkdv_bf16_t<128, true, true>(a, p, s) : launch_dkdv_bf16_t<128, false, true>(a, p, s);
+    }
+    if (D == 64)
+      return g ? launch_dkdv_bf16_t<64, true, false>(a, p, s) : launch_dkdv_bf16_t<64, false, false>(a, p, s);
+    return g ? launch_dkdv_bf16_t<128, true, false>(a, p, s) : launch_dkdv_bf16_t<128, false, false>(a, p, s);
   }
   dim3 grid(T, B * H);
   if (D == 64)

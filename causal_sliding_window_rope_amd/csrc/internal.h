@@ -55,10 +55,15 @@ size_t bwd_workspace_bytes(int B, int T, int H, int D, bool bf16);
 // major), dQ (query-block major).
 hipError_t launch_bwd_pre(const AttnShape& a, const void* o, const void* dO, const float* lse,
                           void* ws, bool bf16, hipStream_t s);
+// ds: nullptr, or (bf16 only) the dS^T buffer of dsbuf.h, which the kernel then also fills.
 hipError_t launch_bwd_dkdv(const AttnShape& a, const void* q, const void* k, const void* v,
                            const void* ve, const float* gate, const float* lse, const void* dO,
                            void* dk, void* dv, void* dve, float* dgate, void* ws, bool bf16,
-                           hipStream_t s);
+                           hipStream_t s, void* ds = nullptr);
+// dq = scale * dS K from the dS^T buffer the dK/dV kernel stored (bf16 only).
+size_t ds_buffer_bytes(int B, int T, int H, int window);
+hipError_t launch_dq_from_ds(const AttnShape& a, const void* k, const void* ds, void* dq,
+                             hipStream_t s);
 hipError_t launch_bwd_dq(const AttnShape& a, const void* q, const void* k, const void* v,
                          const void* ve, const float* gate, const float* lse, const void* dO,
                          void* dq, void* ws, bool bf16, hipStream_t s);

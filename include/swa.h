@@ -210,6 +210,49 @@ int swa_bwd(const void* q, const void* k, const void* v, const void* ve, const f
             size_t ws_bytes, int B, int T, int H, int D, int window, float scale, swa_dtype dtype,
             void* stream);
 
+/*
+ * The backward with the score gradient stored ("GPT-2 124M 复现" §19: the backward recomputes
+ * S and P from the saved row statistics; here that recomputation runs once, in the dK/dV
+ * kernel, and the bf16 dS it forms for dK is kept in the workspace for dq = scale * dS k).
+ * Same results as swa_bwd up to float rounding order, bitwise repeatable (no atomics).
+ *
+ * swa_bwd_ds_workspace_size — bytes of its workspace: swa_bwd's row terms rounded up to 256
+ *   bytes, then (bf16) the dS chunks: B*H*nkb*min(nkb, (W + 126)/128 + 1) * 32 KiB with
+ *   nkb = ceil(T/128) and W the window clamped to T (d24 layer, B=16, H=12, T=2048: 0.91 GB at
+ *   W = 1024, 1.61 GB at W = 2048). window as in swa_bwd; 0 for invalid sizes or windows. For
+ *   float32 nothing is stored and no chunk bytes are added.
+ */
+size_t swa_bwd_ds_workspace_size(int B, int T, int H, int D, int window, swa_dtype dtype);
+
+/*
+ * swa_bwd_ds — swa_bwd on that workspace (device, >= swa_bwd_ds_workspace_size() bytes for
+ *   this window, 256-byte aligned, clobbered). bf16: row terms (as swa_bwd_preprocess), then
+ *   dK/dV storing dS, then dq from the stored dS. float32: the recomputing kernels of swa_bwd.
+ *   Other arguments and outputs as swa_bwd.
+ */
+int swa_bwd_ds(const void* q, const void* k, const void* v, const void* ve, const float* gate,
+               const int* ve_ids, int ve_rows, const int* doc_bounds, const void* o,
+               const float* lse, const void* dO, void* dq, void* dk, void* dv, void* dve,
+               float* dgate, void* workspace, size_t ws_bytes, int B, int T, int H, int D,
+               int window, float scale, swa_dtype dtype, void* stream);
+
+/*
+ * Stages of swa_bwd_ds (bfloat16 only; SWA_ERR_UNSUPPORTED for float32), one workspace sized by
+ * swa_bwd_ds_workspace_size for the same sizes and window, in this order on one stream:
+ *   swa_bwd_preprocess (the row terms; it uses the first swa_bwd_workspace_size bytes),
+ *   swa_bwd_dkdv_ds — swa_bwd_dkdv that also stores dS (arguments as swa_bwd_dkdv),
+ *   swa_bwd_dq_ds   — dq = scale * dS k from the stored dS: k (B,T,H,D) bf16 read, doc_bounds
+ *                     as given to the other stages (NULL or the same), dq (B,T,H,D) written.
+ */
+int swa_bwd_dkdv_ds(const void* q, const void* k, const void* v, const void* ve,
+                    const float* gate, const int* ve_ids, int ve_rows, const int* doc_bounds,
+                    const float* lse, const void* dO, void* dk, void* dv, void* dve, float* dgate,
+                    void* workspace, size_t ws_bytes, int B, int T, int H, int D, int window,
+                    float scale, swa_dtype dtype, void* stream);
+int swa_bwd_dq_ds(const void* k, const int* doc_bounds, void* dq, void* workspace,
+                  size_t ws_bytes, int B, int T, int H, int D, int window, float scale,
+                  swa_dtype dtype, void* stream);
+
 /* Bytes of device scratch that swa_bwd_noalloc holds per GPU (its largest workspace). */
 #define SWA_NOALLOC_SCRATCH_BYTES (16u << 20)
 

@@ -67,10 +67,11 @@ def announce(*parts):
     sys.stdout.flush()
 
 
-def gpu_layer(x: dict, wl, window: int, fused_gate: bool = True):
+def gpu_layer(x: dict, wl, window: int, fused_gate: bool = True, bwd: str = "recompute"):
     """Whole layer on the GPU: prologue, optional gate, swa_fwd, swa_bwd, prologue backward.
     fused_gate=False takes the materialised route: ve_gate_v writes v_eff, the attention runs
-    without the gate, ve_gate_dv turns dv_eff into dve and dgate."""
+    without the gate, ve_gate_dv turns dv_eff into dve and dgate. bwd="ds" runs the backward
+    with the score gradient stored (swa_bwd_ds) instead of swa_bwd."""
     dt = wl.dtype
     q, k, v, dO = (dev(x[n], dt) for n in ("q", "k", "v", "dO"))
     cs = sw.rope_table(wl.T, wl.D, wl.base)
@@ -99,8 +100,9 @@ def gpu_layer(x: dict, wl, window: int, fused_gate: bool = True):
     fgate = gate if ve is not None else None
     o, lse = sw.swa_fwd(qn, kn, v, window, wl.scale, ve=ve, gate=fgate, doc_bounds=bounds,
                         ve_ids=ve_ids)
-    grads = sw.swa_bwd(qn, kn, v, o, lse, dO, window, wl.scale, ve=ve, gate=fgate,
-                       doc_bounds=bounds, ve_ids=ve_ids)
+    bwd_fn = sw.swa_bwd_ds if bwd == "ds" else sw.swa_bwd
+    grads = bwd_fn(qn, kn, v, o, lse, dO, window, wl.scale, ve=ve, gate=fgate,
+                   doc_bounds=bounds, ve_ids=ve_ids)
     if wl.gate and not fused_gate:
         grads = tuple(grads) + sw.ve_gate_dv(grads[2], ve_kernel[0], gate, ve_ids=ve_kernel[1])
     dqn, dkn, dv = grads[:3]
