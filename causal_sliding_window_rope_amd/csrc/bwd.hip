@@ -293,8 +293,8 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dkdv_bf16_kernel(Params 
   auto store_pending = [&]() __attribute__((always_inline)) {
     if constexpr (STORE_DS) {
       if (pend_off >= 0) {
-        __builtin_amdgcn_raw_buffer_store_b128(pend0, ds_rsrc, ds_voff, pend_off, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(pend1, ds_rsrc, ds_voff + 16u, pend_off, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(pend0, ds_rsrc, ds_voff, pend_off, 2);
+        __builtin_amdgcn_raw_buffer_store_b128(pend1, ds_rsrc, ds_voff + 16u, pend_off, 2);
       }
     }
   };

@@ -148,9 +148,9 @@ __global__ void __launch_bounds__(64 * NW, 2) dq_ds_kernel(Params p) {
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<char*>(chunk), 0, live(st, 2 * hh + cc) ? dsb::CHUNK_BYTES : 0, 0x00020000);
       dst[2 * cc + 0] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 16u * lane, 0, 0));
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 16u * lane, 0, 2));
       dst[2 * cc + 1] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 16u * lane + 1024u, 0, 0));
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 16u * lane + 1024u, 0, 2));
     }
   };
   // issue_k: this wave's share of the K tile of step st into registers (lane l of wave load I
