@@ -18,7 +18,8 @@
 //    query order, matched by the transposing LDS reads of the dO and Q tiles).
 //  * Query tiles are double-buffered in LDS by asynchronous global->LDS copies; 32-query
 //    halves that lie wholly outside a wave's keys' windows are skipped by that wave.
-//  * Workgroup order: all key blocks of one (b, h) on one XCD.
+//  * Workgroup order: all key blocks of one (b, h) on one XCD; small full-causal grids longest
+//    first across heads (lpt_block).
 //  * Value-embedding gate: v_eff = v + gate * ve is formed in fp32 when the V rows are loaded;
 //    the epilogue writes dv = dv_eff, dve = gate * dv_eff and dgate = sum_d dv_eff * ve.
 #include "common.h"
@@ -125,6 +126,7 @@ struct Params {
   bf16* ds;      // stored dS^T (dsbuf.h), written by the STORE_DS instantiation
   int nslot;     // query-tile slots per key block in ds
   int B, T, H, window, nkb;
+  int lpt;       // longest-first order across heads (lpt_order)
   float c;       // scale * log2(e)
   float scale;
 };
@@ -191,11 +193,18 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dkdv_bf16_kernel(Params 
   const int g = lane >> 4, j = lane & 15;
   const int T = p.T, H = p.H, W = p.window;
 
-  const int nblk = gridDim.x;
-  int L = blockIdx.x;
-  if ((nblk & 7) == 0) L = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
-  const int bh = L / p.nkb;
-  const int kbk = L - bh * p.nkb;
+  int bh, kbk;   // key block kbk of (b, h); the first key blocks see the most queries
+  if (p.lpt) {
+    const int2 br = lpt_block(p.nkb);
+    bh = br.x;
+    kbk = br.y;
+  } else {
+    const int nblk = gridDim.x;
+    int L = blockIdx.x;
+    if ((nblk & 7) == 0) L = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+    bh = L / p.nkb;
+    kbk = L - bh * p.nkb;
+  }
   const int b = bh / H, h = bh - b * H;
   const size_t head0 = ((size_t)b * T * H + h) * D;
   const size_t rs = (size_t)H * D;
@@ -684,6 +693,7 @@ hipError_t launch_bwd_dkdv(const AttnShape& a, const void* q, const void* k, con
     p.ve_ids = a.ve_ids; p.ve_rows = a.ve_rows; p.dve_tab = (float*)dve;
     p.B = B; p.T = T; p.H = H; p.window = a.window;
     p.nkb = (T + bwdk::BNK - 1) / bwdk::BNK;
+    p.lpt = lpt_order(a) ? 1 : 0;
     p.c = a.scale * kLog2e;
     p.scale = a.scale;
     p.ds = (bf16*)ds;

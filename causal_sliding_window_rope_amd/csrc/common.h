@@ -143,6 +143,14 @@ template <int D> __device__ __forceinline__ int swz(int r);
 template <> __device__ __forceinline__ int swz<128>(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 template <> __device__ __forceinline__ int swz<64>(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 
+// Block (bh, r) of a grid of nper blocks per head in longest-first order (lpt_order in
+// internal.h): workgroup ids go to the eight XCDs in turn; XCD x holds heads x * hpx .. + hpx - 1
+// and issues rank r = 0 (a head's largest block) of each of them before rank 1.
+__device__ __forceinline__ int2 lpt_block(int nper) {
+  const int hpx = (int)(gridDim.x >> 3) / nper, j = (int)(blockIdx.x >> 3), r = j / hpx;
+  return make_int2((int)(blockIdx.x & 7) * hpx + (j - r * hpx), r);
+}
+
 // Scheduling fence: the compiler may not move instructions across it. Used to bound how far
 // ahead LDS loads are hoisted (each hoisted load keeps its result registers live).
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }

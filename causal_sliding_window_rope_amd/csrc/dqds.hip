@@ -50,6 +50,7 @@ struct Params {
   const int* bounds;   // per-token document [start, end) (document masking only)
   bf16* dq;
   int B, T, H, window, nkb, nslot, nqt;
+  int lpt;   // longest-first order across heads (lpt_order)
   float scale;
 };
 
@@ -81,13 +82,20 @@ __global__ void __launch_bounds__(64 * NW, 2) dq_ds_kernel(Params p) {
   // XCD-aware order (the query tiles of one (b, h) share that XCD's L2 for K), most key blocks
   // first, heads in the reverse of the order the dK/dV kernel wrote them, so that the chunks
   // written last (still in the memory-side cache) are read first.
-  const int nblk = gridDim.x;
-  int L = blockIdx.x;
-  if ((nblk & 7) == 0) L = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
-  L = nblk - 1 - L;
-  L = (L / p.nqt) * p.nqt + (p.nqt - 1 - L % p.nqt);   // keep the longest tiles first
-  const int bh = L / p.nqt;
-  const int qt = p.nqt - 1 - (L - bh * p.nqt);
+  int bh, qt;
+  if (p.lpt) {   // small full-causal grids: longest first across heads
+    const int2 br = lpt_block(p.nqt);
+    bh = br.x;
+    qt = p.nqt - 1 - br.y;
+  } else {
+    const int nblk = gridDim.x;
+    int L = blockIdx.x;
+    if ((nblk & 7) == 0) L = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+    L = nblk - 1 - L;
+    L = (L / p.nqt) * p.nqt + (p.nqt - 1 - L % p.nqt);   // keep the longest tiles first
+    bh = L / p.nqt;
+    qt = p.nqt - 1 - (L - bh * p.nqt);
+  }
   const int b = bh / H, h = bh - b * H;
   const size_t head0 = ((size_t)b * T * H + h) * D;
   const size_t rs = (size_t)H * D;
@@ -293,6 +301,7 @@ hipError_t launch_dq_from_ds(const AttnShape& a, const void* k, const void* ds, 
   p.nkb = dsb::nkb(a.T);
   p.nslot = dsb::nslot(a.T, a.window);
   p.nqt = (a.T + dqs::BM - 1) / dqs::BM;
+  p.lpt = lpt_order(a) ? 1 : 0;
   p.scale = a.scale;
   return a.D == 64 ? dqs::launch_t<64>(a, p, s) : dqs::launch_t<128>(a, p, s);
 }

@@ -18,7 +18,7 @@
 //  * Tiles wholly outside a wave's causal window are skipped; only tiles that straddle the
 //    diagonal, the window's lower edge or the sequence end evaluate the mask.
 //  * Workgroup order: all query blocks of one (b, h) run on one XCD (K/V reuse in that XCD's
-//    L2), longest blocks first.
+//    L2), longest blocks first; small full-causal grids longest first across heads (lpt_block).
 //  * Optional value-embedding gate: v_eff = v + gate * ve is formed in fp32 while the V tile is
 //    staged into LDS, so v_eff never touches HBM.
 #include "common.h"
@@ -48,6 +48,7 @@ struct Params {
   int ve_rows;
   bf16* o; float* lse;
   int B, T, H, window, nqb;
+  int lpt;      // longest-first order across heads (lpt_order)
   float c;      // scale * log2(e)
 };
 
@@ -255,11 +256,18 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(Params p) {
   const int T = p.T, H = p.H, W = p.window;
 
   // XCD-aware, longest-first block order.
-  const int nblk = gridDim.x;
-  int L = blockIdx.x;
-  if ((nblk & 7) == 0) L = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
-  const int bh = L / p.nqb;
-  const int qb = p.nqb - 1 - (L - bh * p.nqb);
+  int bh, qb;
+  if (p.lpt) {
+    const int2 br = lpt_block(p.nqb);
+    bh = br.x;
+    qb = p.nqb - 1 - br.y;
+  } else {
+    const int nblk = gridDim.x;
+    int L = blockIdx.x;
+    if ((nblk & 7) == 0) L = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+    bh = L / p.nqb;
+    qb = p.nqb - 1 - (L - bh * p.nqb);
+  }
   const int b = bh / H, h = bh - b * H;
   const size_t head0 = ((size_t)b * T * H + h) * D;   // element (b, 0, h, 0)
   const bf16* kbase = p.k + head0;
@@ -407,6 +415,7 @@ static hipError_t launch_fwd_bf16_t(const AttnShape& a, const void* q, const voi
   p.gate = gate; p.bounds = a.bounds; p.o = (bf16*)o; p.lse = lse;
   p.B = a.B; p.T = a.T; p.H = a.H; p.window = a.window;
   p.nqb = (a.T + fwdk::BM - 1) / fwdk::BM;
+  p.lpt = lpt_order(a) ? 1 : 0;
   p.c = a.scale * kLog2e;
   const unsigned blocks = (unsigned)p.nqb * a.B * a.H;
   if (a.bounds)

@@ -17,6 +17,18 @@ struct AttnShape {
   int ve_rows = 0;
 };
 
+// Longest-first block order for small full-causal grids. With window >= T the work of a block
+// grows with its position along the sequence, and a grid of a few workgroups per slot ends on a
+// long tail when the blocks of one head are issued together. When the per-head tiles that the
+// blocks re-read (2 D-wide bf16 rows per position) of all heads an XCD holds fit in its 4 MiB
+// L2, the kernels instead issue, on each XCD, the largest block of every head first, then the
+// second largest, and so on. Larger grids keep one head's blocks together for L2 reuse.
+inline bool lpt_order(const AttnShape& a) {
+  const long bh = (long)a.B * a.H;
+  return a.window >= a.T && a.bounds == nullptr && bh % 8 == 0 &&
+         (bh / 8) * a.T * a.D * 4 <= (4l << 20);
+}
+
 hipError_t launch_doc_bounds(const int* doc_id, int* bounds, int B, int T, hipStream_t s);
 
 hipError_t launch_rope_table(float* cos_sin, int T, int D, double base, hipStream_t s);
