@@ -159,6 +159,9 @@ def run_bench(args):
             raise sw.SwaError(name, st, lib.swa_last_error().decode())
 
     fused_gate = args.fused_gate
+    # the query half of the prologue inside swa_fwd_qnorm / swa_bwd_dq_ds_qnorm (stored-dS
+    # backward only); the prologue calls then run on k alone
+    qnorm = stored_ds and not args.no_qnorm
 
     def step(rec):
         stream = sw._stream()   # the current stream: the capture stream when recording a graph
@@ -166,8 +169,8 @@ def run_bench(args):
         for li, t in enumerate(layers):
             bounds, ids = t.get("bounds"), t.get("ids")
             rows = 0 if ids is None else t["ve"].shape[0]
-            call("rope_qknorm_fwd", P(t["q"]), P(t["k"]), P(cs), P(t["qn"]), P(t["kn"]), B, T, H, D,
-                 1e-6, sw.SWA_BF16, stream)
+            call("rope_qknorm_fwd", None if qnorm else P(t["q"]), P(t["k"]), P(cs),
+                 None if qnorm else P(t["qn"]), P(t["kn"]), B, T, H, D, 1e-6, sw.SWA_BF16, stream)
             ve = gate = fids = None
             frows, v = 0, t["v"]
             if cfg["gate"] and fused_gate:
@@ -179,9 +182,14 @@ def run_bench(args):
                      P(ids), rows, P(t["veff"]), B, T, H, D, sw.SWA_BF16, stream)
                 v = t["veff"]
             if rec: rec["fwd"][li][0].record()
-            call("swa_fwd", P(t["qn"]), P(t["kn"]), P(v), P(ve), P(gate), P(fids), frows,
-                 P(bounds), P(t["o"]), P(t["lse"]),
-                 B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
+            if qnorm:
+                call("swa_fwd_qnorm", P(t["q"]), P(cs), 1e-6, P(t["kn"]), P(v), P(ve), P(gate),
+                     P(fids), frows, P(bounds), P(t["qn"]), P(t["o"]), P(t["lse"]),
+                     B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
+            else:
+                call("swa_fwd", P(t["qn"]), P(t["kn"]), P(v), P(ve), P(gate), P(fids), frows,
+                     P(bounds), P(t["o"]), P(t["lse"]),
+                     B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
             if rec: rec["fwd"][li][1].record()
         # backward, layers in reverse
         for li in reversed(range(len(layers))):
@@ -206,8 +214,12 @@ def run_bench(args):
                      frows, P(bounds), P(t["lse"]), P(t["dO"]), P(g["dkn"]), P(g["dv"]), P(dve),
                      P(dgate), P(ws), nws, B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
                 if rec: rec["bwd"][li][2].record()
-                call("swa_bwd_dq_ds", P(t["kn"]), P(bounds), P(g["dqn"]), P(ws), nws,
-                     B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
+                if qnorm:   # dq w.r.t. the raw q straight from the dQ kernel
+                    call("swa_bwd_dq_ds_qnorm", P(t["kn"]), P(bounds), P(t["q"]), P(cs), 1e-6,
+                         P(g["dq"]), P(ws), nws, B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
+                else:
+                    call("swa_bwd_dq_ds", P(t["kn"]), P(bounds), P(g["dqn"]), P(ws), nws,
+                         B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
                 if rec: rec["bwd"][li][3].record()
             else:
                 # dQ first: its kernel also writes the row terms (delta, lse) that dK/dV reads
@@ -222,7 +234,8 @@ def run_bench(args):
                      P(t["dO"]), P(g["dkn"]), P(g["dv"]), P(dve), P(dgate), P(ws), nws,
                      B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
                 if rec: rec["bwd"][li][3].record()
-            call("rope_qknorm_bwd", P(t["q"]), P(t["k"]), P(cs), P(g["dqn"]), P(g["dkn"]), P(g["dq"]),
+            call("rope_qknorm_bwd", None if qnorm else P(t["q"]), P(t["k"]), P(cs),
+                 None if qnorm else P(g["dqn"]), P(g["dkn"]), None if qnorm else P(g["dq"]),
                  P(g["dk"]), B, T, H, D, 1e-6, sw.SWA_BF16, stream)
             if cfg["gate"]:
                 if not fused_gate:   # dve, dgate from dv_eff (= dv)
@@ -331,6 +344,8 @@ def run_bench(args):
             "swa_bwd_tflops_credited": round(bwd_tf, 2),
             "backward": ("row terms, dK/dV storing dS, dQ from the stored dS" if stored_ds
                          else "dQ with the row terms, then dK/dV (S and dP recomputed twice)"),
+            "query_prologue": ("inside the forward and dQ kernels (their times include it)"
+                               if qnorm else "in the prologue calls"),
             "swa_bwd_dkdv_tflops_executed": round(kv_flop / (kv_ms / args.steps * 1e-3) / 1e12, 2),
             "swa_bwd_dq_tflops_executed": round(dq_flop / (dq_ms / args.steps * 1e-3) / 1e12, 2),
             "swa_fwd_ms_per_step": round(fwd_ms / args.steps, 4),
@@ -349,10 +364,10 @@ def run_bench(args):
 # source files each timed kernel is compiled from (a change to any of them invalidates the
 # committed counter figures for that kernel)
 KERNEL_SOURCES = {
-    "fwd_bf16_kernel": ("fwd.hip", "common.h"),
+    "fwd_bf16_kernel": ("fwd.hip", "common.h", "rope_row.h"),
     "dkdv_bf16_kernel": ("bwd.hip", "common.h", "dsbuf.h"),
     "dq_bf16_kernel": ("dq.hip", "common.h"),
-    "dq_ds_kernel": ("dqds.hip", "common.h", "dsbuf.h"),
+    "dq_ds_kernel": ("dqds.hip", "common.h", "dsbuf.h", "rope_row.h"),
 }
 
 
@@ -713,6 +728,10 @@ def main():
     ap.add_argument("--bwd", choices=("ds", "recompute"), default="ds",
                     help="backward: dS stored by the dK/dV kernel and read by the dQ kernel "
                          "(default), or S and dP recomputed in both")
+    ap.add_argument("--no-qnorm", action="store_true",
+                    help="with --bwd ds: run the query half of the RoPE/QK-norm prologue (and of "
+                         "its backward) in the separate prologue calls instead of inside the "
+                         "forward and dQ kernels (swa_fwd_qnorm, swa_bwd_dq_ds_qnorm)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="only run a plain device-to-device copy of this many MiB 5 times (used to "
                          "scale HBM byte counters under rocprofv3), then exit")

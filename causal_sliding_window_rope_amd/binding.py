@@ -45,6 +45,9 @@ SIGNATURES = {
     "swa_bwd_dkdv_ds": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _S,
                              _I, _I, _I, _I, _I, _F, _I, _P]),
     "swa_bwd_dq_ds": (_I, [_P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "swa_fwd_qnorm": (_I, [_P, _P, _F, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                           _F, _I, _P]),
+    "swa_bwd_dq_ds_qnorm": (_I, [_P, _P, _P, _P, _F, _P, _P, _S, _I, _I, _I, _I, _I, _F, _I, _P]),
     "swa_bwd_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                              _I, _I, _I, _I, _I, _F, _I, _P]),
     "swa_bwd_preprocess": (_I, [_P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _P]),
@@ -133,24 +136,30 @@ def rope_table(T: int, D: int, base: float = 10000.0, device="cuda") -> torch.Te
 
 
 def rope_qknorm_fwd(q, k, cos_sin, eps: float = 1e-6):
-    B, T, H, D = q.shape
+    """(qn, kn); q=None processes k only and returns (None, kn)."""
+    B, T, H, D = k.shape
     for t, n in ((q, "q"), (k, "k")):
-        _check(t, n, (B, T, H, D), q.dtype)
+        if t is not None:
+            _check(t, n, (B, T, H, D), k.dtype)
     _check(cos_sin, "cos_sin", (T, D // 2, 2), torch.float32)
-    qn, kn = torch.empty_like(q), torch.empty_like(k)
+    qn = None if q is None else torch.empty_like(q)
+    kn = torch.empty_like(k)
     _call("rope_qknorm_fwd", _ptr(q), _ptr(k), _ptr(cos_sin), _ptr(qn), _ptr(kn), B, T, H, D,
-          float(eps), _dt(q), _stream())
+          float(eps), _dt(k), _stream())
     return qn, kn
 
 
 def rope_qknorm_bwd(q, k, cos_sin, dqn, dkn, eps: float = 1e-6):
-    B, T, H, D = q.shape
+    """(dq, dk); q=None and dqn=None process k only and return (None, dk)."""
+    B, T, H, D = k.shape
     for t, n in ((q, "q"), (k, "k"), (dqn, "dqn"), (dkn, "dkn")):
-        _check(t, n, (B, T, H, D), q.dtype)
+        if t is not None:
+            _check(t, n, (B, T, H, D), k.dtype)
     _check(cos_sin, "cos_sin", (T, D // 2, 2), torch.float32)
-    dq, dk = torch.empty_like(q), torch.empty_like(k)
+    dq = None if q is None else torch.empty_like(q)
+    dk = torch.empty_like(k)
     _call("rope_qknorm_bwd", _ptr(q), _ptr(k), _ptr(cos_sin), _ptr(dqn), _ptr(dkn), _ptr(dq),
-          _ptr(dk), B, T, H, D, float(eps), _dt(q), _stream())
+          _ptr(dk), B, T, H, D, float(eps), _dt(k), _stream())
     return dq, dk
 
 
@@ -259,6 +268,43 @@ def swa_fwd(q, k, v, window: int, scale: float | None = None, ve=None, gate=None
           _ptr(o),
           _ptr(lse), B, T, H, D, int(window), float(scale), _dt(q), _stream())
     return o, lse
+
+
+def swa_fwd_qnorm(q, cos_sin, k, v, window: int, scale: float | None = None,
+                  eps: float = 1e-6, ve=None, gate=None, doc_bounds=None, ve_ids=None):
+    """swa_fwd with the query prologue inside the kernel: q raw, k normalised; returns
+    (qn, o, lse)."""
+    B, T, H, D = q.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, (B, T, H, D), q.dtype)
+    _check(cos_sin, "cos_sin", (T, D // 2, 2), torch.float32)
+    ids, rows = _ve_table(ve, gate, ve_ids, B, T, H, D, q.dtype)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    qn, o = torch.empty_like(q), torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    if doc_bounds is not None:
+        _check(doc_bounds, "doc_bounds", (B, T, 2), torch.int32)
+    _call("swa_fwd_qnorm", _ptr(q), _ptr(cos_sin), float(eps), _ptr(k), _ptr(v), _ptr(ve),
+          _ptr(gate), ids, rows, _ptr(doc_bounds), _ptr(qn), _ptr(o), _ptr(lse), B, T, H, D,
+          int(window), float(scale), _dt(q), _stream())
+    return qn, o, lse
+
+
+def swa_bwd_dq_ds_qnorm(k, q, cos_sin, workspace, window: int, scale: float | None = None,
+                        eps: float = 1e-6, doc_bounds=None, out=None):
+    """dq w.r.t. the raw queries q from the dS stored in `workspace` by swa_bwd_dkdv_ds."""
+    B, T, H, D = k.shape
+    for t, n in ((q, "q"), (k, "k")):
+        _check(t, n, (B, T, H, D), k.dtype)
+    _check(cos_sin, "cos_sin", (T, D // 2, 2), torch.float32)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    dq = torch.empty_like(q) if out is None else out
+    if doc_bounds is not None:
+        _check(doc_bounds, "doc_bounds", (B, T, 2), torch.int32)
+    _call("swa_bwd_dq_ds_qnorm", _ptr(k), _ptr(doc_bounds), _ptr(q), _ptr(cos_sin), float(eps),
+          _ptr(dq), _ptr(workspace), workspace.numel() * workspace.element_size(), B, T, H, D,
+          int(window), float(scale), _dt(k), _stream())
+    return dq
 
 
 def swa_bwd_workspace_size(B: int, T: int, H: int, D: int, dtype: torch.dtype) -> int:

@@ -137,11 +137,13 @@ int rope_qknorm_fwd(const void* q, const void* k, const float* cos_sin, void* qn
                     int T, int H, int D, float eps, swa_dtype dtype, void* stream) {
   const char* fn = "rope_qknorm_fwd";
   SWA_TRY(check_shape(fn, B, T, H, D, dtype));
-  SWA_TRY(need(fn, "q", q)); SWA_TRY(need(fn, "k", k)); SWA_TRY(need(fn, "cos_sin", cos_sin));
-  SWA_TRY(need(fn, "qn", qn)); SWA_TRY(need(fn, "kn", kn));
+  SWA_TRY(need(fn, "k", k)); SWA_TRY(need(fn, "cos_sin", cos_sin)); SWA_TRY(need(fn, "kn", kn));
+  if ((q == nullptr) != (qn == nullptr))
+    return fail(SWA_ERR_INVALID_ARG, "%s: q and qn must be given together (both NULL: k only)", fn);
+  if (q) { SWA_TRY(need(fn, "q", q)); SWA_TRY(need(fn, "qn", qn)); }
   if (!(std::isfinite(eps) && eps >= 0.f))
     return fail(SWA_ERR_INVALID_ARG, "%s: eps must be finite and >= 0", fn);
-  if (qn == q || qn == k || kn == q || kn == k)
+  if ((q && (qn == q || qn == k || kn == q)) || kn == k)
     return fail(SWA_ERR_INVALID_ARG, "%s: outputs may not alias inputs", fn);
   return hip_status(swa::launch_rope_qknorm_fwd(q, k, cos_sin, qn, kn, B, T, H, D, eps,
                                                 dtype == SWA_BF16, (hipStream_t)stream), fn);
@@ -152,9 +154,12 @@ int rope_qknorm_bwd(const void* q, const void* k, const float* cos_sin, const vo
                     swa_dtype dtype, void* stream) {
   const char* fn = "rope_qknorm_bwd";
   SWA_TRY(check_shape(fn, B, T, H, D, dtype));
-  SWA_TRY(need(fn, "q", q)); SWA_TRY(need(fn, "k", k)); SWA_TRY(need(fn, "cos_sin", cos_sin));
-  SWA_TRY(need(fn, "dqn", dqn)); SWA_TRY(need(fn, "dkn", dkn));
-  SWA_TRY(need(fn, "dq", dq)); SWA_TRY(need(fn, "dk", dk));
+  SWA_TRY(need(fn, "k", k)); SWA_TRY(need(fn, "cos_sin", cos_sin));
+  SWA_TRY(need(fn, "dkn", dkn)); SWA_TRY(need(fn, "dk", dk));
+  if ((q == nullptr) != (dqn == nullptr) || (q == nullptr) != (dq == nullptr))
+    return fail(SWA_ERR_INVALID_ARG,
+                "%s: q, dqn and dq must be given together (all NULL: k only)", fn);
+  if (q) { SWA_TRY(need(fn, "q", q)); SWA_TRY(need(fn, "dqn", dqn)); SWA_TRY(need(fn, "dq", dq)); }
   if (!(std::isfinite(eps) && eps >= 0.f))
     return fail(SWA_ERR_INVALID_ARG, "%s: eps must be finite and >= 0", fn);
   return hip_status(swa::launch_rope_qknorm_bwd(q, k, cos_sin, dqn, dkn, dq, dk, B, T, H, D, eps,
@@ -273,6 +278,33 @@ int swa_fwd(const void* q, const void* k, const void* v, const void* ve, const f
   SWA_TRY(check_window_scale(fn, window, scale, T, &a.window));
   return hip_status(swa::launch_fwd(a, q, k, v, ve, gate, o, lse, dtype == SWA_BF16,
                                     (hipStream_t)stream), fn);
+}
+
+int swa_fwd_qnorm(const void* q, const float* cos_sin, float eps, const void* k, const void* v,
+                  const void* ve, const float* gate, const int* ve_ids, int ve_rows,
+                  const int* doc_bounds, void* qn, void* o, float* lse, int B, int T, int H, int D,
+                  int window, float scale, swa_dtype dtype, void* stream) {
+  const char* fn = "swa_fwd_qnorm";
+  if (dtype != SWA_BF16)
+    return fail(SWA_ERR_UNSUPPORTED, "%s: the fused query prologue is bfloat16 only", fn);
+  SWA_TRY(check_shape(fn, B, T, H, D, dtype));
+  SWA_TRY(need(fn, "q", q)); SWA_TRY(need(fn, "cos_sin", cos_sin)); SWA_TRY(need(fn, "k", k));
+  SWA_TRY(need(fn, "v", v)); SWA_TRY(need(fn, "qn", qn)); SWA_TRY(need(fn, "o", o));
+  SWA_TRY(need(fn, "lse", lse));
+  if (!(std::isfinite(eps) && eps >= 0.f))
+    return fail(SWA_ERR_INVALID_ARG, "%s: eps must be finite and >= 0", fn);
+  if (qn == q || qn == k || qn == v || qn == o)
+    return fail(SWA_ERR_INVALID_ARG, "%s: qn may not alias q, k, v or o", fn);
+  if ((ve == nullptr) != (gate == nullptr))
+    return fail(SWA_ERR_INVALID_ARG, "%s: ve and gate must be given together", fn);
+  SWA_TRY(opt(fn, "ve", ve)); SWA_TRY(opt(fn, "doc_bounds", doc_bounds));
+  swa::AttnShape a{B, T, H, D, 0, scale};
+  a.bounds = doc_bounds;
+  SWA_TRY(check_ve_table(fn, ve, ve_ids, ve_rows, H, D, &a));
+  SWA_TRY(check_window_scale(fn, window, scale, T, &a.window));
+  const swa::QNorm qnorm{q, cos_sin, eps, qn};
+  return hip_status(swa::launch_fwd(a, nullptr, k, v, ve, gate, o, lse, true,
+                                    (hipStream_t)stream, &qnorm), fn);
 }
 
 size_t swa_bwd_workspace_size(int B, int T, int H, int D, swa_dtype dtype) {
@@ -405,6 +437,29 @@ int swa_bwd_dq_ds(const void* k, const int* doc_bounds, void* dq, void* workspac
   SWA_TRY(check_ws_ds(fn, workspace, ws_bytes, B, T, H, D, a.window, dtype));
   return hip_status(swa::launch_dq_from_ds(a, k, ds_part(workspace, B, T, H, D, dtype), dq,
                                            (hipStream_t)stream), fn);
+}
+
+int swa_bwd_dq_ds_qnorm(const void* k, const int* doc_bounds, const void* q,
+                        const float* cos_sin, float eps, void* dq, void* workspace,
+                        size_t ws_bytes, int B, int T, int H, int D, int window, float scale,
+                        swa_dtype dtype, void* stream) {
+  const char* fn = "swa_bwd_dq_ds_qnorm";
+  if (dtype != SWA_BF16)
+    return fail(SWA_ERR_UNSUPPORTED, "%s: the stored-dS stages are bfloat16 only", fn);
+  SWA_TRY(check_shape(fn, B, T, H, D, dtype));
+  SWA_TRY(need(fn, "k", k)); SWA_TRY(need(fn, "q", q)); SWA_TRY(need(fn, "cos_sin", cos_sin));
+  SWA_TRY(need(fn, "dq", dq));
+  SWA_TRY(opt(fn, "doc_bounds", doc_bounds));
+  if (!(std::isfinite(eps) && eps >= 0.f))
+    return fail(SWA_ERR_INVALID_ARG, "%s: eps must be finite and >= 0", fn);
+  if (dq == q || dq == k) return fail(SWA_ERR_INVALID_ARG, "%s: dq may not alias q or k", fn);
+  swa::AttnShape a{B, T, H, D, 0, scale};
+  a.bounds = doc_bounds;
+  SWA_TRY(check_window_scale(fn, window, scale, T, &a.window));
+  SWA_TRY(check_ws_ds(fn, workspace, ws_bytes, B, T, H, D, a.window, dtype));
+  const swa::QNorm qnorm{q, cos_sin, eps, nullptr};
+  return hip_status(swa::launch_dq_from_ds(a, k, ds_part(workspace, B, T, H, D, dtype), dq,
+                                           (hipStream_t)stream, &qnorm), fn);
 }
 
 int swa_bwd_preprocess(const void* o, const void* dO, const float* lse, void* workspace,

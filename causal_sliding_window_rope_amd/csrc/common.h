@@ -90,6 +90,7 @@ __device__ __forceinline__ float half_swap(float v) {
 template <typename T> using lds_t = __attribute__((address_space(3))) T;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 // Asynchronous 16-byte global -> LDS copy in its buffer form (buffer_load_dwordx4 ... lds):
 // lane l of the wave reads resource + voff bytes and writes lds_base + 16*l bytes (lds_base

@@ -24,6 +24,7 @@
 #include "common.h"
 #include "dsbuf.h"
 #include "internal.h"
+#include "rope_row.h"
 
 namespace swa {
 namespace dqs {
@@ -49,6 +50,7 @@ struct Params {
   const char* ds;
   const int* bounds;   // per-token document [start, end) (document masking only)
   bf16* dq;
+  const bf16* qraw; const float* cs; float eps;   // QN kernels: the query prologue's backward
   int B, T, H, window, nkb, nslot, nqt;
   int lpt;   // longest-first order across heads (lpt_order)
   float scale;
@@ -61,7 +63,7 @@ __device__ __forceinline__ void ds_store_b128(lds_t<char>* p, u32x4 v) {
   asm volatile("ds_write_b128 %0, %1" : : "v"((unsigned)(size_t)p), "v"(v) : "memory");
 }
 
-template <int D, bool DOC>
+template <int D, bool DOC, bool QN>
 __global__ void __launch_bounds__(64 * NW, 2) dq_ds_kernel(Params p) {
   using C = Cfg<D>;
   constexpr int NDB = D / 32;
@@ -259,6 +261,57 @@ __global__ void __launch_bounds__(64 * NW, 2) dq_ds_kernel(Params p) {
 
   wait_vmem();   // the surplus loads of the last steps land before the wave ends
 
+  if constexpr (QN) {
+    // The backward of the query prologue (RMS norm, then RoPE) in the row layout of
+    // rope_row.h, so that dq is bitwise what rope_qknorm_bwd computes from this kernel's bf16
+    // dq_hat: each wave puts its dq_hat rows, rounded to bf16 and 16-byte chunks XOR-swizzled,
+    // into the K buffers (rows 0-63 in kb0, 64-127 in kb1) once every wave is done with them;
+    // then TPR lanes per row read a row back with the raw q row and the angles of its position
+    // and write dq.
+    using RW = RowWord<bf16>;
+    constexpr int VPT = RW::VPT, TPR = D / VPT, RPP = 64 * NW / TPR, NP = BM / RPP;
+    const int lr = tid % TPR;
+    const bool second = lr >= TPR / 2;
+    // the raw rows and angles of every pass first (rows past the end re-read the last row and
+    // store nothing); their latency overlaps the staging below
+    RW x[NP];
+    float c[NP][VPT], s[NP][VPT];
+#pragma unroll
+    for (int pass = 0; pass < NP; ++pass) {
+      const int t = min(q0 + pass * RPP + tid / TPR, T - 1);
+      x[pass].load(p.qraw + head0 + (size_t)t * rs + lr * VPT);
+      load_cs<VPT>(p.cs, t, D / 2, (lr % (TPR / 2)) * VPT, c[pass], s[pass]);
+    }
+    __syncthreads();
+    if (myq < T) {
+      const int rl = (32 * wave + l32) & 63;
+      lds_t<bf16>* rowp = kslot(wave >> 1) + rl * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const u32x2 w = {pack_bf2(dqacc[db][4 * a + 0] * p.scale, dqacc[db][4 * a + 1] * p.scale),
+                           pack_bf2(dqacc[db][4 * a + 2] * p.scale, dqacc[db][4 * a + 3] * p.scale)};
+          const int ch = 4 * db + a;   // 16-byte chunk of d = 32 db + 8 a
+          *reinterpret_cast<lds_t<u32x2>*>(rowp + 8 * (ch ^ swz<D>(rl)) + 4 * hi) = w;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int pass = 0; pass < NP; ++pass) {
+      const int r = pass * RPP + tid / TPR;
+      const int t = q0 + r;
+      const int rl = r & 63;
+      const u32x4 gw = *reinterpret_cast<const lds_t<u32x4>*>(kslot(r >> 6) + rl * D +
+                                                               8 * (lr ^ swz<D>(rl)));
+      RW g, out;
+      g.v[0] = bf_lo(gw[0]); g.v[1] = bf_hi(gw[0]); g.v[2] = bf_lo(gw[1]); g.v[3] = bf_hi(gw[1]);
+      g.v[4] = bf_lo(gw[2]); g.v[5] = bf_hi(gw[2]); g.v[6] = bf_lo(gw[3]); g.v[7] = bf_hi(gw[3]);
+      rope_norm_row_bwd<VPT, TPR, D>(x[pass].v, g.v, c[pass], s[pass], second, p.eps, out.v);
+      if (t < T) out.store(p.dq + head0 + (size_t)t * rs + lr * VPT);
+    }
+    return;
+  }
   // dq row myq: lane holds d = 32 db + 8 a + 4 hi + (0..3)
   if (myq < T) {
     bf16* op = p.dq + head0 + (size_t)myq * rs;
@@ -274,13 +327,13 @@ __global__ void __launch_bounds__(64 * NW, 2) dq_ds_kernel(Params p) {
   }
 }
 
-template <int D>
+template <int D, bool QN>
 static hipError_t launch_t(const AttnShape& a, const Params& p, hipStream_t s) {
   const unsigned blocks = (unsigned)p.nqt * a.B * a.H;
   if (a.bounds)
-    hipLaunchKernelGGL((dq_ds_kernel<D, true>), dim3(blocks), dim3(64 * NW), 0, s, p);
+    hipLaunchKernelGGL((dq_ds_kernel<D, true, QN>), dim3(blocks), dim3(64 * NW), 0, s, p);
   else
-    hipLaunchKernelGGL((dq_ds_kernel<D, false>), dim3(blocks), dim3(64 * NW), 0, s, p);
+    hipLaunchKernelGGL((dq_ds_kernel<D, false, QN>), dim3(blocks), dim3(64 * NW), 0, s, p);
   return hipGetLastError();
 }
 
@@ -291,7 +344,7 @@ size_t ds_buffer_bytes(int B, int T, int H, int window) {
 }
 
 hipError_t launch_dq_from_ds(const AttnShape& a, const void* k, const void* ds, void* dq,
-                             hipStream_t s) {
+                             hipStream_t s, const QNorm* qnorm) {
   dqs::Params p;
   p.k = (const bf16*)k;
   p.ds = (const char*)ds;
@@ -303,7 +356,12 @@ hipError_t launch_dq_from_ds(const AttnShape& a, const void* k, const void* ds, 
   p.nqt = (a.T + dqs::BM - 1) / dqs::BM;
   p.lpt = lpt_order(a) ? 1 : 0;
   p.scale = a.scale;
-  return a.D == 64 ? dqs::launch_t<64>(a, p, s) : dqs::launch_t<128>(a, p, s);
+  p.qraw = qnorm ? (const bf16*)qnorm->q : nullptr;
+  p.cs = qnorm ? qnorm->cs : nullptr;
+  p.eps = qnorm ? qnorm->eps : 0.f;
+  if (qnorm)
+    return a.D == 64 ? dqs::launch_t<64, true>(a, p, s) : dqs::launch_t<128, true>(a, p, s);
+  return a.D == 64 ? dqs::launch_t<64, false>(a, p, s) : dqs::launch_t<128, false>(a, p, s);
 }
 
 }  // namespace swa

@@ -23,6 +23,7 @@
 //    staged into LDS, so v_eff never touches HBM.
 #include "common.h"
 #include "internal.h"
+#include "rope_row.h"
 
 namespace swa {
 
@@ -47,6 +48,7 @@ struct Params {
   const int* ve_ids;   // value-embedding table rows per token (table mode only)
   int ve_rows;
   bf16* o; float* lse;
+  const bf16* qraw; const float* cs; float eps; bf16* qn;   // QN kernels: the query prologue
   int B, T, H, window, nqb;
   int lpt;      // longest-first order across heads (lpt_order)
   float c;      // scale * log2(e)
@@ -240,7 +242,7 @@ __device__ __forceinline__ void tile_step(WaveState<D>& ws, const bf16x8* qreg,
     for (int sp = 0; sp < 2; ++sp) ws.oacc[db] = mfma32(va1[db][sp], pb[1][sp], ws.oacc[db]);
 }
 
-template <int D, bool GATE, bool DOC>
+template <int D, bool GATE, bool DOC, bool QN>
 __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(Params p) {
   using C = Cfg<D>;
   constexpr int NDB = D / 32;
@@ -277,9 +279,61 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(Params p) {
   const int qw = q0 + wave * 32;      // first query of this wave
   const int myq = qw + l32;           // this lane's query row
 
+  const RowRange rr = row_range<DOC>(p.bounds, b, T, W, myq);
+  int lo_q0 = max(q0 - W + 1, 0);   // first key any query of the workgroup sees
+  if constexpr (DOC) lo_q0 = max(lo_q0, p.bounds[2 * ((size_t)b * T + q0)]);
+  const int kt_lo = lo_q0 / BN;
+  const int kt_hi = min(T - 1, q0 + BM - 1) / BN;
+
+  Tiles<D, GATE> tl;
+  tl.init(H, wave, lane);
+  if constexpr (QN) tl.load(p, kbase, vbase, K0, V0, kt_lo, tid);   // overlaps the query prologue
+
   // Q^T operand: 8 bf16 of row myq per k-step, held for the whole kernel.
   bf16x8 qreg[NKS];
-  {
+  if constexpr (QN) {
+    // The query rows' prologue (RoPE, then RMS norm) in the row layout of rope_row.h, so that
+    // each normalised row is bitwise what rope_qknorm_fwd writes: TPR lanes per row, RPP rows
+    // per pass. Each row goes to qn and, 16-byte chunks XOR-swizzled as in the K tiles, to the
+    // second K/V buffers (rows 0-63 in K1, 64-127 in V1; unused until the second key tile),
+    // from which every wave then reads its 32 rows as the Q^T operand.
+    using RW = RowWord<bf16>;
+    constexpr int VPT = RW::VPT, TPR = D / VPT, RPP = 64 * NW / TPR, NP = BM / RPP;
+    const int lr = tid % TPR;
+    const bool second = lr >= TPR / 2;
+    // every pass's row and angle loads first (rows past the end re-read the last row and
+    // store nothing), then the arithmetic
+    RW x[NP];
+    float c[NP][VPT], s[NP][VPT];
+#pragma unroll
+    for (int pass = 0; pass < NP; ++pass) {
+      const int t = min(q0 + pass * RPP + tid / TPR, T - 1);
+      x[pass].load(p.qraw + head0 + (size_t)t * H * D + lr * VPT);
+      load_cs<VPT>(p.cs, t, D / 2, (lr % (TPR / 2)) * VPT, c[pass], s[pass]);
+    }
+#pragma unroll
+    for (int pass = 0; pass < NP; ++pass) {
+      const int r = pass * RPP + tid / TPR;
+      const int t = q0 + r;
+      RW out;
+      rope_norm_row<VPT, TPR, D>(x[pass].v, c[pass], s[pass], second, p.eps, out.v);
+      u32x4 w = {0u, 0u, 0u, 0u};   // rows past the end: zero operands
+      if (t < T) {
+        out.store(p.qn + head0 + (size_t)t * H * D + lr * VPT);
+        w = (u32x4){pack_bf2(out.v[0], out.v[1]), pack_bf2(out.v[2], out.v[3]),
+                    pack_bf2(out.v[4], out.v[5]), pack_bf2(out.v[6], out.v[7])};
+      }
+      const int rl = r & 63;
+      *reinterpret_cast<lds_t<u32x4>*>((r < 64 ? K1 : V1) + rl * D + 8 * (lr ^ swz<D>(rl))) = w;
+    }
+    __syncthreads();
+    const lds_t<bf16>* qs = (wave < 2 ? K1 : V1);
+    const int rl = 32 * (wave & 1) + l32;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      qreg[ks] = *reinterpret_cast<const lds_t<bf16x8>*>(qs + rl * D +
+                                                          8 * ((2 * ks + hi) ^ swz<D>(rl)));
+  } else {
     const bf16* qp = p.q + head0 + (size_t)min(myq, T - 1) * H * D + 8 * hi;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
@@ -289,11 +343,6 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(Params p) {
     }
   }
 
-  const RowRange rr = row_range<DOC>(p.bounds, b, T, W, myq);
-  int lo_q0 = max(q0 - W + 1, 0);   // first key any query of the workgroup sees
-  if constexpr (DOC) lo_q0 = max(lo_q0, p.bounds[2 * ((size_t)b * T + q0)]);
-  const int kt_lo = lo_q0 / BN;
-  const int kt_hi = min(T - 1, q0 + BM - 1) / BN;
 
   WaveState<D> ws;
 #pragma unroll
@@ -319,9 +368,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(Params p) {
     }
   }
 
-  Tiles<D, GATE> tl;
-  tl.init(H, wave, lane);
-  tl.load(p, kbase, vbase, K0, V0, kt_lo, tid);
+  if constexpr (!QN) tl.load(p, kbase, vbase, K0, V0, kt_lo, tid);
   wait_vmem();
   __syncthreads();
   // Two tiles per trip so that each LDS buffer is named statically.
@@ -405,10 +452,10 @@ __global__ void __launch_bounds__(64) fwd_f32_kernel(const float* __restrict__ q
   if (lane == 0) lse[(size_t)bh * T + i] = m + logf(l);
 }
 
-template <int D, bool GATE>
+template <int D, bool GATE, bool QN>
 static hipError_t launch_fwd_bf16_t(const AttnShape& a, const void* q, const void* k, const void* v,
                                     const void* ve, const float* gate, void* o, float* lse,
-                                    hipStream_t s) {
+                                    hipStream_t s, const QNorm* qnorm) {
   fwdk::Params p;
   p.q = (const bf16*)q; p.k = (const bf16*)k; p.v = (const bf16*)v; p.ve = (const bf16*)ve;
   p.ve_ids = a.ve_ids; p.ve_rows = a.ve_rows;
@@ -417,27 +464,41 @@ static hipError_t launch_fwd_bf16_t(const AttnShape& a, const void* q, const voi
   p.nqb = (a.T + fwdk::BM - 1) / fwdk::BM;
   p.lpt = lpt_order(a) ? 1 : 0;
   p.c = a.scale * kLog2e;
+  p.qraw = nullptr; p.cs = nullptr; p.eps = 0.f; p.qn = nullptr;
+  if (QN) {
+    p.qraw = (const bf16*)qnorm->q; p.cs = qnorm->cs; p.eps = qnorm->eps;
+    p.qn = (bf16*)qnorm->qn;
+  }
   const unsigned blocks = (unsigned)p.nqb * a.B * a.H;
   if (a.bounds)
-    hipLaunchKernelGGL((fwdk::fwd_bf16_kernel<D, GATE, true>), dim3(blocks), dim3(64 * fwdk::NW), 0,
-                       s, p);
+    hipLaunchKernelGGL((fwdk::fwd_bf16_kernel<D, GATE, true, QN>), dim3(blocks),
+                       dim3(64 * fwdk::NW), 0, s, p);
   else
-    hipLaunchKernelGGL((fwdk::fwd_bf16_kernel<D, GATE, false>), dim3(blocks), dim3(64 * fwdk::NW), 0,
-                       s, p);
+    hipLaunchKernelGGL((fwdk::fwd_bf16_kernel<D, GATE, false, QN>), dim3(blocks),
+                       dim3(64 * fwdk::NW), 0, s, p);
   return hipGetLastError();
+}
+
+template <int D, bool GATE>
+static hipError_t launch_fwd_bf16_q(const AttnShape& a, const void* q, const void* k,
+                                    const void* v, const void* ve, const float* gate, void* o,
+                                    float* lse, hipStream_t s, const QNorm* qnorm) {
+  return qnorm ? launch_fwd_bf16_t<D, GATE, true>(a, q, k, v, ve, gate, o, lse, s, qnorm)
+               : launch_fwd_bf16_t<D, GATE, false>(a, q, k, v, ve, gate, o, lse, s, qnorm);
 }
 
 hipError_t launch_fwd(const AttnShape& a, const void* q, const void* k, const void* v,
                       const void* ve, const float* gate, void* o, float* lse, bool is_bf16,
-                      hipStream_t s) {
+                      hipStream_t s, const QNorm* qnorm) {
   if (is_bf16) {
     const bool g = gate != nullptr;
     if (a.D == 64)
-      return g ? launch_fwd_bf16_t<64, true>(a, q, k, v, ve, gate, o, lse, s)
-               : launch_fwd_bf16_t<64, false>(a, q, k, v, ve, gate, o, lse, s);
-    return g ? launch_fwd_bf16_t<128, true>(a, q, k, v, ve, gate, o, lse, s)
-             : launch_fwd_bf16_t<128, false>(a, q, k, v, ve, gate, o, lse, s);
+      return g ? launch_fwd_bf16_q<64, true>(a, q, k, v, ve, gate, o, lse, s, qnorm)
+               : launch_fwd_bf16_q<64, false>(a, q, k, v, ve, gate, o, lse, s, qnorm);
+    return g ? launch_fwd_bf16_q<128, true>(a, q, k, v, ve, gate, o, lse, s, qnorm)
+             : launch_fwd_bf16_q<128, false>(a, q, k, v, ve, gate, o, lse, s, qnorm);
   }
+  if (qnorm) return hipErrorInvalidValue;   // the fused query prologue is bf16 only
   dim3 grid(a.T, a.B * a.H);
   if (a.D == 64)
     hipLaunchKernelGGL(fwd_f32_kernel<64>, grid, dim3(64), 0, s, (const float*)q, (const float*)k,

@@ -17,6 +17,16 @@ struct AttnShape {
   int ve_rows = 0;
 };
 
+// The query half of the RoPE -> RMS QK-norm prologue run inside an attention kernel: q is the
+// raw (B,T,H,D) input, cs the rope_table angles, eps the norm's epsilon; qn (the forward) is
+// where the normalised rows go.
+struct QNorm {
+  const void* q;
+  const float* cs;
+  float eps;
+  void* qn;
+};
+
 // Longest-first block order for small full-causal grids. With window >= T the work of a block
 // grows with its position along the sequence, and a grid of a few workgroups per slot ends on a
 // long tail when the blocks of one head are issued together. When the per-head tiles that the
@@ -58,9 +68,11 @@ hipError_t launch_ve_gate_bwd(const void* x, int ldx, const float* Wg, const flo
                               const float* dgate, float* dWg, void* dx32, void* ws, int B, int T,
                               int H, bool bf16, hipStream_t s);
 
+// qnorm: NULL, or (bf16 only) q is ignored and the kernel normalises the raw rows qnorm->q
+// itself, writing them to qnorm->qn (bitwise what rope_qknorm_fwd writes).
 hipError_t launch_fwd(const AttnShape& a, const void* q, const void* k, const void* v,
                       const void* ve, const float* gate, void* o, float* lse, bool bf16,
-                      hipStream_t s);
+                      hipStream_t s, const QNorm* qnorm = nullptr);
 
 size_t bwd_workspace_bytes(int B, int T, int H, int D, bool bf16);
 // Backward in three stages on one workspace: row terms (-delta, -lse*log2e), dK/dV (key-block
@@ -74,8 +86,11 @@ hipError_t launch_bwd_dkdv(const AttnShape& a, const void* q, const void* k, con
                            hipStream_t s, void* ds = nullptr);
 // dq = scale * dS K from the dS^T buffer the dK/dV kernel stored (bf16 only).
 size_t ds_buffer_bytes(int B, int T, int H, int window);
+// qnorm: NULL, or dq is the gradient w.r.t. the raw rows qnorm->q (the query prologue's
+// backward applied to this kernel's bf16 dq_hat, bitwise what rope_qknorm_bwd gives).
 hipError_t launch_dq_from_ds(const AttnShape& a, const void* k, const void* ds, void* dq,
-                             hipStream_t s);
+                             hipStream_t s,
+                             const QNorm* qnorm = nullptr);
 hipError_t launch_bwd_dq(const AttnShape& a, const void* q, const void* k, const void* v,
                          const void* ve, const float* gate, const float* lse, const void* dO,
                          void* dq, void* ws, bool bf16, hipStream_t s);

@@ -12,6 +12,7 @@
 // (two row reads per row) keeps one row per lane group, which measured faster for it.
 #include "common.h"
 #include "internal.h"
+#include "rope_row.h"
 
 namespace swa {
 
@@ -34,72 +35,6 @@ hipError_t launch_rope_table(float* cos_sin, int T, int D, double base, hipStrea
   return hipGetLastError();
 }
 
-// One 128-bit word of a row: VPT elements as floats.
-template <typename E> struct RowWord {
-  static constexpr int VPT = 16 / sizeof(E);
-  float v[VPT];
-  __device__ __forceinline__ void load(const E* p) {
-    const uint4 w = *reinterpret_cast<const uint4*>(p);
-    if constexpr (sizeof(E) == 4) {
-      v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y);
-      v[2] = __uint_as_float(w.z); v[3] = __uint_as_float(w.w);
-    } else {
-      v[0] = bf_lo(w.x); v[1] = bf_hi(w.x); v[2] = bf_lo(w.y); v[3] = bf_hi(w.y);
-      v[4] = bf_lo(w.z); v[5] = bf_hi(w.z); v[6] = bf_lo(w.w); v[7] = bf_hi(w.w);
-    }
-  }
-  __device__ __forceinline__ void store(E* p) const {
-    uint4 w;
-    if constexpr (sizeof(E) == 4) {
-      w.x = __float_as_uint(v[0]); w.y = __float_as_uint(v[1]);
-      w.z = __float_as_uint(v[2]); w.w = __float_as_uint(v[3]);
-    } else {
-      w.x = pack_bf2(v[0], v[1]); w.y = pack_bf2(v[2], v[3]);
-      w.z = pack_bf2(v[4], v[5]); w.w = pack_bf2(v[6], v[7]);
-    }
-    *reinterpret_cast<uint4*>(p) = w;
-  }
-};
-
-// Sum over the TPR lanes that hold one row (TPR is a power of two <= 64, groups aligned).
-template <int TPR>
-__device__ __forceinline__ float row_sum(float x) {
-  return group_sum<TPR>(x);
-}
-
-// The rotation partner's value: lane j ^ (TPR/2) of the row group (a DPP row rotation for
-// 16-lane groups, a shuffle otherwise).
-template <int TPR>
-__device__ __forceinline__ float partner(float x) {
-  if constexpr (TPR == 16) return dpp_mov<0x128>(x);
-  else return xor_shfl(x, TPR / 2);
-}
-
-// cos/sin of the VPT angle slots starting at pair index i0 for position t.
-template <int VPT>
-__device__ __forceinline__ void load_cs(const float* __restrict__ cs, int t, int half, int i0,
-                                        float* c, float* s) {
-  const float4* p = reinterpret_cast<const float4*>(cs + 2 * ((size_t)t * half + i0));
-#pragma unroll
-  for (int e = 0; e < VPT / 2; ++e) {
-    const float4 w = p[e];
-    c[2 * e] = w.x; s[2 * e] = w.y; c[2 * e + 1] = w.z; s[2 * e + 1] = w.w;
-  }
-}
-
-// Rotate one word: lanes in the first half of the row hold x1 (pair index i < D/2), lanes in
-// the second half hold x2; `other` is the partner lane's word. sign = +1 forward, -1 transpose.
-template <int VPT>
-__device__ __forceinline__ void rotate(float* y, const float* x, const float* other, const float* c,
-                                       const float* s, bool second_half, float sign) {
-#pragma unroll
-  for (int e = 0; e < VPT; ++e) {
-    const float ss = sign * s[e];
-    // first half: y1 = x1 c - x2 s ; second half: y2 = x1 s + x2 c
-    y[e] = second_half ? fmaf(other[e], ss, x[e] * c[e]) : fmaf(-other[e], ss, x[e] * c[e]);
-  }
-}
-
 // Forward: one wave per (tensor, token). Its 64 / TPR row groups (TPR lanes, one 128-bit word
 // each) take consecutive heads, so each load instruction covers a contiguous run of rows, and
 // walk the H heads with stride 64 / TPR, U rows per group with their loads issued together.
@@ -113,13 +48,13 @@ constexpr int kRowsInFlight = 4;
 template <typename E, int D, bool OUT8>
 __global__ void __launch_bounds__(256) rope_qknorm_fwd_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const float* __restrict__ cs,
-    void* __restrict__ qn, void* __restrict__ kn, int tokens, int T, int H, float eps) {
+    void* __restrict__ qn, void* __restrict__ kn, int tokens, int T, int H, float eps, int wv0) {
   using W = RowWord<E>;
   constexpr int VPT = W::VPT, TPR = D / VPT, HALF_T = TPR / 2, U = kRowsInFlight;
   constexpr int GPW = 64 / TPR;   // row groups per wave = head stride
   const int lane_in_row = threadIdx.x % TPR;
   const int gw = (threadIdx.x % 64) / TPR;
-  const int wv = blockIdx.x * 4 + threadIdx.x / 64;
+  const int wv = wv0 + blockIdx.x * 4 + threadIdx.x / 64;   // wv0 = tokens: k only
   if (wv >= 2 * tokens) return;  // whole waves exit together
   const bool is_k = wv >= tokens;
   const int bt = is_k ? wv - tokens : wv;
@@ -139,18 +74,8 @@ __global__ void __launch_bounds__(256) rope_qknorm_fwd_kernel(
     for (int u = 0; u < U; ++u) {
       if (h0 + GPW * u >= H) break;
       const size_t off = ((size_t)bt * H + h0 + GPW * u) * D + lane_in_row * VPT;
-      float other[VPT], y[VPT];
-#pragma unroll
-      for (int e = 0; e < VPT; ++e) other[e] = partner<TPR>(x[u].v[e]);
-      rotate<VPT>(y, x[u].v, other, c, s, second, 1.0f);
-      float ss = 0.f;
-#pragma unroll
-      for (int e = 0; e < VPT; ++e) ss = fmaf(y[e], y[e], ss);
-      ss = row_sum<TPR>(ss);
-      const float rinv = 1.0f / sqrtf(ss / (float)D + eps);
       W out;
-#pragma unroll
-      for (int e = 0; e < VPT; ++e) out.v[e] = y[e] * rinv;
+      rope_norm_row<VPT, TPR, D>(x[u].v, c, s, second, eps, out.v);
       if constexpr (OUT8) {
         unsigned w[VPT / 4];
 #pragma unroll
@@ -173,11 +98,11 @@ template <typename E, int D>
 __global__ void __launch_bounds__(256) rope_qknorm_bwd_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const float* __restrict__ cs,
     const E* __restrict__ dqn, const E* __restrict__ dkn, E* __restrict__ dq, E* __restrict__ dk,
-    int rows_per_tensor, int T, int H, float eps) {
+    int rows_per_tensor, int T, int H, float eps, int row0) {
   using W = RowWord<E>;
   constexpr int VPT = W::VPT, TPR = D / VPT, HALF_T = TPR / 2;
   const int lane_in_row = threadIdx.x % TPR;
-  const int row = blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  const int row = row0 + blockIdx.x * (256 / TPR) + threadIdx.x / TPR;   // row0 > 0: k only
   if (row >= 2 * rows_per_tensor) return;
   const bool is_k = row >= rows_per_tensor;
   const int r = is_k ? row - rows_per_tensor : row;
@@ -187,28 +112,10 @@ __global__ void __launch_bounds__(256) rope_qknorm_bwd_kernel(
   x.load((is_k ? k : q) + off);
   g.load((is_k ? dkn : dqn) + off);
   const bool second = lane_in_row >= HALF_T;
-  float c[VPT], s[VPT], other[VPT], u[VPT];
+  float c[VPT], s[VPT];
   load_cs<VPT>(cs, t, D / 2, (lane_in_row % HALF_T) * VPT, c, s);
-#pragma unroll
-  for (int e = 0; e < VPT; ++e) other[e] = partner<TPR>(x.v[e]);
-  rotate<VPT>(u, x.v, other, c, s, second, 1.0f);
-  float ss = 0.f;
-#pragma unroll
-  for (int e = 0; e < VPT; ++e) ss = fmaf(u[e], u[e], ss);
-  ss = row_sum<TPR>(ss);
-  const float rinv = 1.0f / sqrtf(ss / (float)D + eps);
-  float dot = 0.f;
-#pragma unroll
-  for (int e = 0; e < VPT; ++e) dot = fmaf(u[e] * rinv, g.v[e], dot);
-  dot = row_sum<TPR>(dot);
-  const float dd = dot / (float)D;
-  float du[VPT];
-#pragma unroll
-  for (int e = 0; e < VPT; ++e) du[e] = rinv * (g.v[e] - u[e] * rinv * dd);
-#pragma unroll
-  for (int e = 0; e < VPT; ++e) other[e] = partner<TPR>(du[e]);
   W out;
-  rotate<VPT>(out.v, du, other, c, s, second, -1.0f);
+  rope_norm_row_bwd<VPT, TPR, D>(x.v, g.v, c, s, second, eps, out.v);
   out.store((is_k ? dk : dq) + off);
 }
 
@@ -216,9 +123,10 @@ template <typename E, int D, bool OUT8 = false>
 static hipError_t launch_fwd_t(const void* q, const void* k, const float* cs, void* qn, void* kn,
                                int B, int T, int H, float eps, hipStream_t s) {
   const int tokens = B * T;
-  const int blocks = (2 * tokens + 3) / 4;   // one wave per (tensor, token)
+  const int wv0 = q ? 0 : tokens;   // no q: the k rows only
+  const int blocks = (2 * tokens - wv0 + 3) / 4;   // one wave per (tensor, token)
   hipLaunchKernelGGL((rope_qknorm_fwd_kernel<E, D, OUT8>), dim3(blocks), dim3(256), 0, s,
-                     (const E*)q, (const E*)k, cs, qn, kn, tokens, T, H, eps);
+                     (const E*)q, (const E*)k, cs, qn, kn, tokens, T, H, eps, wv0);
   return hipGetLastError();
 }
 
@@ -240,10 +148,11 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const float* cs, co
   constexpr int TPR = D / (16 / sizeof(E));
   const int rows = B * T * H;
   const int rpb = 256 / TPR;
-  const int blocks = (2 * rows + rpb - 1) / rpb;
+  const int row0 = q ? 0 : rows;   // no q: the k rows only
+  const int blocks = (2 * rows - row0 + rpb - 1) / rpb;
   hipLaunchKernelGGL((rope_qknorm_bwd_kernel<E, D>), dim3(blocks), dim3(256), 0, s,
                      (const E*)q, (const E*)k, cs, (const E*)dqn, (const E*)dkn, (E*)dq, (E*)dk,
-                     rows, T, H, eps);
+                     rows, T, H, eps, row0);
   return hipGetLastError();
 }
 

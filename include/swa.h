@@ -88,7 +88,8 @@ int rope_table(float* cos_sin, int T, int D, double base, void* stream);
  * The 1/sqrt(D) score scale is not applied here; swa_fwd/swa_bwd take it as `scale`.
  *   q, k   : device (B,T,H,D) dtype, read.         qn, kn: device (B,T,H,D) dtype, written.
  *   cos_sin: device table from rope_table(T, D).   eps >= 0 finite.
- * qn/kn may not alias q/k.
+ * qn/kn may not alias q/k. q and qn may both be NULL: then only k is processed (for callers
+ * that run the query half inside swa_fwd_qnorm).
  */
 int rope_qknorm_fwd(const void* q, const void* k, const float* cos_sin, void* qn, void* kn,
                     int B, int T, int H, int D, float eps, swa_dtype dtype, void* stream);
@@ -100,6 +101,8 @@ int rope_qknorm_fwd(const void* q, const void* k, const float* cos_sin, void* qn
  *   q, k  : device (B,T,H,D) dtype, the raw pre-RoPE inputs, read.
  *   dqn, dkn: device (B,T,H,D) dtype, gradients w.r.t. q_hat, k_hat, read.
  *   dq, dk: device (B,T,H,D) dtype, written (may alias dqn/dkn).
+ * q, dqn and dq may all be NULL: then only k is processed (for callers that run the query half
+ * inside swa_bwd_dq_ds_qnorm).
  */
 int rope_qknorm_bwd(const void* q, const void* k, const float* cos_sin, const void* dqn,
                     const void* dkn, void* dq, void* dk, int B, int T, int H, int D, float eps,
@@ -184,6 +187,22 @@ int swa_fwd(const void* q, const void* k, const void* v, const void* ve, const f
             const int* ve_ids, int ve_rows, const int* doc_bounds, void* o, float* lse, int B,
             int T, int H, int D, int window, float scale, swa_dtype dtype, void* stream);
 
+/*
+ * swa_fwd_qnorm — swa_fwd with the query half of the prologue run inside the attention kernel
+ *   (bfloat16 only; SWA_ERR_UNSUPPORTED for float32): each workgroup normalises its own query
+ *   rows (RoPE then RMS norm, "从4万美元到73美元" §2.2, §2.1, as rope_qknorm_fwd) before its
+ *   key loop, so q_hat is formed without a separate pass over q.
+ *   q: device (B,T,H,D) bf16, the RAW queries, read.   cos_sin, eps: as rope_qknorm_fwd.
+ *   k: the normalised keys (rope_qknorm_fwd with q = NULL).   qn: device (B,T,H,D) bf16,
+ *   written: the normalised queries, bitwise what rope_qknorm_fwd writes (the backward needs
+ *   them). o, lse: bitwise what swa_fwd(qn, k, ...) writes. Other arguments as swa_fwd;
+ *   qn may not alias q, k, v or o.
+ */
+int swa_fwd_qnorm(const void* q, const float* cos_sin, float eps, const void* k, const void* v,
+                  const void* ve, const float* gate, const int* ve_ids, int ve_rows,
+                  const int* doc_bounds, void* qn, void* o, float* lse, int B, int T, int H, int D,
+                  int window, float scale, swa_dtype dtype, void* stream);
+
 /* Bytes of workspace swa_bwd needs: the row terms -delta and -lse*log2(e), each (B,H,T) float32,
  * 256-byte aligned inside the block and followed by 512 bytes of slack. */
 size_t swa_bwd_workspace_size(int B, int T, int H, int D, swa_dtype dtype);
@@ -252,6 +271,19 @@ int swa_bwd_dkdv_ds(const void* q, const void* k, const void* v, const void* ve,
 int swa_bwd_dq_ds(const void* k, const int* doc_bounds, void* dq, void* workspace,
                   size_t ws_bytes, int B, int T, int H, int D, int window, float scale,
                   swa_dtype dtype, void* stream);
+
+/*
+ * swa_bwd_dq_ds_qnorm — swa_bwd_dq_ds followed, inside the same kernel, by the query half of
+ *   the prologue's backward (rope_qknorm_bwd): each workgroup turns its dq_hat rows (rounded
+ *   to bf16 as swa_bwd_dq_ds stores them) into the gradient w.r.t. the raw queries.
+ *   q: device (B,T,H,D) bf16, the RAW queries, read.   cos_sin, eps: as rope_qknorm_bwd.
+ *   dq: device (B,T,H,D) bf16, written: bitwise what rope_qknorm_bwd computes for q from
+ *   swa_bwd_dq_ds's output. dq may not alias q or k. Other arguments as swa_bwd_dq_ds.
+ */
+int swa_bwd_dq_ds_qnorm(const void* k, const int* doc_bounds, const void* q,
+                        const float* cos_sin, float eps, void* dq, void* workspace,
+                        size_t ws_bytes, int B, int T, int H, int D, int window, float scale,
+                        swa_dtype dtype, void* stream);
 
 /* Bytes of device scratch that swa_bwd_noalloc holds per GPU (its largest workspace). */
 #define SWA_NOALLOC_SCRATCH_BYTES (16u << 20)

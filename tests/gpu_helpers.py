@@ -67,15 +67,22 @@ def announce(*parts):
     sys.stdout.flush()
 
 
-def gpu_layer(x: dict, wl, window: int, fused_gate: bool = True, bwd: str = "recompute"):
+def gpu_layer(x: dict, wl, window: int, fused_gate: bool = True, bwd: str = "recompute",
+              qnorm: bool = False):
     """Whole layer on the GPU: prologue, optional gate, swa_fwd, swa_bwd, prologue backward.
     fused_gate=False takes the materialised route: ve_gate_v writes v_eff, the attention runs
     without the gate, ve_gate_dv turns dv_eff into dve and dgate. bwd="ds" runs the backward
-    with the score gradient stored (swa_bwd_ds) instead of swa_bwd."""
+    with the score gradient stored (swa_bwd_ds) instead of swa_bwd. qnorm=True (with bwd="ds")
+    runs the query half of the prologue inside the attention kernels (swa_fwd_qnorm,
+    swa_bwd_dq_ds_qnorm) and the prologue calls on k only."""
     dt = wl.dtype
     q, k, v, dO = (dev(x[n], dt) for n in ("q", "k", "v", "dO"))
     cs = sw.rope_table(wl.T, wl.D, wl.base)
-    qn, kn = sw.rope_qknorm_fwd(q, k, cs, wl.eps)
+    if qnorm:
+        assert bwd == "ds"
+        qn, kn = None, sw.rope_qknorm_fwd(None, k, cs, wl.eps)[1]
+    else:
+        qn, kn = sw.rope_qknorm_fwd(q, k, cs, wl.eps)
     out = {"qn": qn, "kn": kn}
     ve = gate = ve_ids = None
     if wl.gate:
@@ -98,15 +105,30 @@ def gpu_layer(x: dict, wl, window: int, fused_gate: bool = True, bwd: str = "rec
         bounds = sw.swa_doc_bounds(torch.from_numpy(x["doc_id"].astype(np.int32)).cuda())
         out["doc_bounds"] = bounds
     fgate = gate if ve is not None else None
-    o, lse = sw.swa_fwd(qn, kn, v, window, wl.scale, ve=ve, gate=fgate, doc_bounds=bounds,
-                        ve_ids=ve_ids)
+    if qnorm:
+        qn, o, lse = sw.swa_fwd_qnorm(q, cs, kn, v, window, wl.scale, eps=wl.eps, ve=ve,
+                                      gate=fgate, doc_bounds=bounds, ve_ids=ve_ids)
+        out["qn"] = qn
+    else:
+        o, lse = sw.swa_fwd(qn, kn, v, window, wl.scale, ve=ve, gate=fgate, doc_bounds=bounds,
+                            ve_ids=ve_ids)
     bwd_fn = sw.swa_bwd_ds if bwd == "ds" else sw.swa_bwd
+    ws = None
+    if qnorm:
+        ws = torch.empty(sw.swa_bwd_ds_workspace_size(wl.B, wl.T, wl.H, wl.D, window,
+                                                      q.dtype), dtype=torch.uint8, device="cuda")
+    kw = dict(stages=True, workspace=ws) if qnorm else {}
     grads = bwd_fn(qn, kn, v, o, lse, dO, window, wl.scale, ve=ve, gate=fgate,
-                   doc_bounds=bounds, ve_ids=ve_ids)
+                   doc_bounds=bounds, ve_ids=ve_ids, **kw)
     if wl.gate and not fused_gate:
         grads = tuple(grads) + sw.ve_gate_dv(grads[2], ve_kernel[0], gate, ve_ids=ve_kernel[1])
     dqn, dkn, dv = grads[:3]
-    dq, dk = sw.rope_qknorm_bwd(q, k, cs, dqn, dkn, wl.eps)
+    if qnorm:
+        dq = sw.swa_bwd_dq_ds_qnorm(kn, q, cs, ws, window, wl.scale, eps=wl.eps,
+                                    doc_bounds=bounds)
+        dk = sw.rope_qknorm_bwd(None, k, cs, None, dkn, wl.eps)[1]
+    else:
+        dq, dk = sw.rope_qknorm_bwd(q, k, cs, dqn, dkn, wl.eps)
     out.update(O=o, lse=lse, dqh=dqn, dkh=dkn, dv=dv, dq=dq, dk=dk)
     if wl.gate:
         out["dve"], out["dgate"] = grads[3], grads[4]

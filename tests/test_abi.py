@@ -156,6 +156,38 @@ def test_swa_bwd_validation(lib):
     assert dq(ve=P, gate=P, ids=P, rows=0) == INVALID   # table mode without rows
 
 
+def test_fused_query_prologue_validation(lib):
+    """swa_fwd_qnorm / swa_bwd_dq_ds_qnorm (the query half of the prologue inside the attention
+    kernels) and the k-only forms of the prologue calls: host-side checks only."""
+    A = ctypes.c_void_p(0x20000)
+
+    def fwd(q=P, cs=P, eps=1e-6, qn=A, dtype=1, W=8):
+        return lib.swa_fwd_qnorm(q, cs, eps, P, P, None, None, None, 0, None, qn, P, P, 2, 64, 3,
+                                 64, W, 0.125, dtype, None)
+
+    assert fwd(dtype=0) == UNSUPPORTED                 # bfloat16 only
+    assert fwd(q=None) == INVALID and fwd(cs=None) == INVALID and fwd(qn=None) == INVALID
+    assert fwd(eps=-1.0) == INVALID
+    assert fwd(qn=P) == INVALID                        # qn aliases q
+    assert fwd(W=0) == INVALID and fwd(q=MIS) == ALIGN
+    nws = lib.swa_bwd_ds_workspace_size(2, 64, 3, 64, 8, 1)
+
+    def dq(q=P, cs=P, eps=1e-6, out=A, ws_bytes=nws, dtype=1):
+        return lib.swa_bwd_dq_ds_qnorm(P, None, q, cs, eps, out, P, ws_bytes, 2, 64, 3, 64, 8,
+                                       0.125, dtype, None)
+
+    assert dq(dtype=0) == UNSUPPORTED
+    assert dq(q=None) == INVALID and dq(cs=None) == INVALID and dq(out=None) == INVALID
+    assert dq(eps=float("nan")) == INVALID
+    assert dq(out=P) == INVALID                        # dq aliases q
+    assert dq(ws_bytes=nws - 1) == WORKSPACE
+    # k only: q and its outputs NULL together
+    assert lib.rope_qknorm_fwd(None, P, P, A, ctypes.c_void_p(0x30000), 1, 8, 1, 64, 1e-6, 1,
+                               None) == INVALID       # qn without q
+    assert lib.rope_qknorm_bwd(None, P, P, None, P, A, ctypes.c_void_p(0x30000), 1, 8, 1, 64,
+                               1e-6, 1, None) == INVALID   # dq without q
+
+
 def test_swa_bwd_noalloc_validation(lib):
     """Checks that run on the host before the scratch is touched: bad arguments, and sizes whose
     workspace would not fit the library's static scratch."""
