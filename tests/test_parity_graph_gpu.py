@@ -71,6 +71,55 @@ def test_layer_graph_replay_matches_eager_and_oracle():
     check("dv", dv, bwd["dv"], "bf16")
 
 
+def test_stored_ds_layer_graph_replay_matches_eager():
+    """The benchmarked route: the prologue on k alone, the forward with the query prologue
+    inside, the stored-dS backward (row terms, dK/dV storing dS, dQ with the query prologue's
+    backward) on one workspace, the prologue backward on k alone. The workspace is filled with
+    NaN bit patterns before each replay: chunks that are never written must never be read."""
+    wl = small_workload(2, 300, 3, 128, 100, "bf16", seed=19)
+    announce("graph replay: stored-dS layer", wl.name)
+    x = make_inputs(wl)
+    t = {n: torch.from_numpy(x[n]).to(torch.bfloat16).cuda() for n in ("q", "k", "v", "dO")}
+    cs = sw.rope_table(wl.T, wl.D, wl.base)
+    ws = torch.empty(sw.swa_bwd_ds_workspace_size(wl.B, wl.T, wl.H, wl.D, wl.window,
+                                                  torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+
+    def layer():
+        kn = sw.rope_qknorm_fwd(None, t["k"], cs, wl.eps)[1]
+        qn, o, lse = sw.swa_fwd_qnorm(t["q"], cs, kn, t["v"], wl.window, wl.scale, eps=wl.eps)
+        _, dkn, dv = sw.swa_bwd_ds(qn, kn, t["v"], o, lse, t["dO"], wl.window, wl.scale,
+                                   workspace=ws, stages=True)
+        dq = sw.swa_bwd_dq_ds_qnorm(kn, t["q"], cs, ws, wl.window, wl.scale, eps=wl.eps)
+        dk = sw.rope_qknorm_bwd(None, t["k"], cs, None, dkn, wl.eps)[1]
+        return o, lse, dq, dk, dv
+
+    eager = [a.clone() for a in layer()]
+    torch.cuda.synchronize()
+    g, outs = _capture(layer)
+    for rep in range(3):
+        for a in outs:
+            a.fill_(float("nan"))
+        ws.view(torch.float32).fill_(float("nan"))
+        (t["q"].float() * 2).sum()  # unrelated eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("O", "lse", "dq", "dk", "dv"), outs, eager):
+            assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager run"
+
+    f = {n: x[n].astype(np.float64) for n in ("q", "k", "v", "dO")}
+    fwd = oracle.layer_fwd(f["q"], f["k"], f["v"], wl.window, base=wl.base, eps=wl.eps,
+                           round_boundary=True)
+    bwd = oracle.layer_bwd(f["q"], f["k"], f["v"], f["dO"], wl.window, fwd, base=wl.base,
+                           eps=wl.eps)
+    o, lse, dq, dk, dv = (host(a) for a in outs)
+    check("O", o, fwd["O"], "bf16")
+    check("lse", lse, fwd["lse"], "bf16", lse=True)
+    check("dq", dq, bwd["dq"], "bf16")
+    check("dk", dk, bwd["dk"], "bf16")
+    check("dv", dv, bwd["dv"], "bf16")
+
+
 def test_decode_step_graph_replay_matches_eager():
     """A decoding step captured once; between replays the program writes the next token's
     q, k, v into the captured input buffers and advances the positions on the device. The
