@@ -15,7 +15,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libswa.so")
+# SWA_LIB names another build of the same library (e.g. one compiled with different options)
+LIB_PATH = os.environ.get("SWA_LIB") or os.path.join(_PKG, "libswa.so")
 
 SWA_F32, SWA_BF16 = 0, 1
 SWA_WINDOW_FULL = -1

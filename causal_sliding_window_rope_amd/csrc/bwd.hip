@@ -138,19 +138,25 @@ struct Params {
   float scale;
 };
 
-// Asynchronous loads of query tile qt (Q, dO rows and the negated row terms) into LDS.
-template <int D>
+// Asynchronous loads of query tile qt (Q, dO rows and the negated row terms) into LDS, part
+// `part` of NPART: the tile's copies are issued in NPART portions spread over the previous
+// tile's units, because a burst of them stalls the wave at issue until the copy path has
+// drained enough of them (it moves far fewer bytes per clock than the matrix cores consume).
+template <int D, int NPART = 1>
 __device__ __forceinline__ void load_qtile(const Params& p, const bf16* qbase, const bf16* obase,
                                            const float* l2base, const float* dlbase,
                                            lds_t<bf16>* Qs, lds_t<bf16>* Os, lds_t<float>* Ls,
-                                           lds_t<float>* Dls, int qt, int wave, int lane) {
+                                           lds_t<float>* Dls, int qt, int wave, int lane,
+                                           int part = 0) {
   using C = Cfg<D>;
+  static_assert(C::NIQ % NPART == 0, "copies split evenly");
+  constexpr int PER = C::NIQ / NPART;
   const size_t rs = (size_t)p.H * D;
   // buffer copies relative to the tile's first row (32-bit lane offsets within one tile)
   const size_t t0 = (size_t)qt * BMQ * rs;
   const __amdgpu_buffer_rsrc_t rq = buf_rsrc(qbase + t0), ro = buf_rsrc(obase + t0);
 #pragma unroll
-  for (int i = 0; i < C::NIQ; ++i) {
+  for (int i = part * PER; i < part * PER + PER; ++i) {
     const int I = wave * C::NIQ + i;
     const int r = I * C::RPI + lane / C::CH;
     const int c = (lane % C::CH) ^ swz<D>(r);
@@ -159,7 +165,7 @@ __device__ __forceinline__ void load_qtile(const Params& p, const bf16* qbase, c
     b2lds16(rq, vo, (lds_t<void>*)(Qs + I * C::RPI * D));
     b2lds16(ro, vo, (lds_t<void>*)(Os + I * C::RPI * D));
   }
-  if (lane < BMQ / 4 && wave < 2) {
+  if (part == 0 && lane < BMQ / 4 && wave < 2) {
     // a tile that runs past the sequence end reads into the next head's row or the workspace
     // slack (see bwd_workspace_bytes); those queries are masked
     const __amdgpu_buffer_rsrc_t rl = buf_rsrc((wave == 0 ? l2base : dlbase) + qt * BMQ);
@@ -316,8 +322,11 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dkdv_bf16_kernel(Params 
   };
 
   // One query tile: recompute S, P, dP, dS in 32-query halves; accumulate dV and dK.
+  // The next tile's copies (into Qn, On, Ln, Dn, if qt + 1 <= qt_hi) are issued a quarter at
+  // the start of each unit, whether or not this wave computes the unit.
   auto tile = [&](const lds_t<bf16>* Qs, const lds_t<bf16>* Os, const lds_t<float>* Ls,
-                  const lds_t<float>* Dls, int qt) {
+                  const lds_t<float>* Dls, int qt, lds_t<bf16>* Qn, lds_t<bf16>* On,
+                  lds_t<float>* Ln, lds_t<float>* Dn) {
     const int q0 = qt * BMQ;
     // S operands of a unit (row term, Q rows): read for unit 0 here and for unit mb + 1 during
     // the dK MFMAs of unit mb
@@ -334,6 +343,9 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dkdv_bf16_kernel(Params 
     read_s_ops(0);
 #pragma unroll
     for (int mb = 0; mb < BMQ / 32; ++mb) {
+      if (qt + 1 <= qt_hi)
+        load_qtile<D, BMQ / 32>(p, qbase, obase, l2base, dlbase, Qn, On, Ln, Dn, qt + 1, wave,
+                                lane, mb);
       const int qm = q0 + 32 * mb;
       const bool skip = (qm + 31 < kw) || (qm > whi1) || (kw >= T);
       if (skip) {
@@ -463,13 +475,11 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dkdv_bf16_kernel(Params 
   wait_vmem();
   __syncthreads();
   for (int qt = qt_lo; qt <= qt_hi; qt += 2) {
-    if (qt + 1 <= qt_hi) load_qtile<D>(p, qbase, obase, l2base, dlbase, Q1, O1, L1, D1, qt + 1, wave, lane);
-    tile(Q0, O0, L0, D0, qt);
+    tile(Q0, O0, L0, D0, qt, Q1, O1, L1, D1);
     if (qt + 1 > qt_hi) break;
     wait_vmem();
     lds_sync();
-    if (qt + 2 <= qt_hi) load_qtile<D>(p, qbase, obase, l2base, dlbase, Q0, O0, L0, D0, qt + 2, wave, lane);
-    tile(Q1, O1, L1, D1, qt + 1);
+    tile(Q1, O1, L1, D1, qt + 1, Q0, O0, L0, D0);
     if (qt + 2 > qt_hi) break;
     wait_vmem();
     lds_sync();
