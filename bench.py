@@ -160,8 +160,13 @@ def run_bench(args):
 
     fused_gate = args.fused_gate
     # the query half of the prologue inside swa_fwd_qnorm / swa_bwd_dq_ds_qnorm (stored-dS
-    # backward only); the prologue calls then run on k alone
-    qnorm = stored_ds and not args.no_qnorm
+    # backward only); the prologue calls then run on k alone. By default where it is measured
+    # faster: at head dim 128 (the d24 layers); at 64 (the GPT-2 layer) each forward workgroup's
+    # prologue loads are a larger share of its short key range and the separate pass wins.
+    if args.qnorm == "auto":
+        qnorm = stored_ds and not args.no_qnorm and D == 128
+    else:
+        qnorm = stored_ds and not args.no_qnorm and args.qnorm == "on"
 
     def step(rec):
         stream = sw._stream()   # the current stream: the capture stream when recording a graph
@@ -728,10 +733,12 @@ def main():
     ap.add_argument("--bwd", choices=("ds", "recompute"), default="ds",
                     help="backward: dS stored by the dK/dV kernel and read by the dQ kernel "
                          "(default), or S and dP recomputed in both")
-    ap.add_argument("--no-qnorm", action="store_true",
+    ap.add_argument("--qnorm", choices=("auto", "on", "off"), default="auto",
                     help="with --bwd ds: run the query half of the RoPE/QK-norm prologue (and of "
-                         "its backward) in the separate prologue calls instead of inside the "
-                         "forward and dQ kernels (swa_fwd_qnorm, swa_bwd_dq_ds_qnorm)")
+                         "its backward) inside the forward and dQ kernels (swa_fwd_qnorm, "
+                         "swa_bwd_dq_ds_qnorm: on) or in the separate prologue calls (off); auto: "
+                         "on at head dim 128, off at 64")
+    ap.add_argument("--no-qnorm", action="store_true", help="the same as --qnorm off")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="only run a plain device-to-device copy of this many MiB 5 times (used to "
                          "scale HBM byte counters under rocprofv3), then exit")

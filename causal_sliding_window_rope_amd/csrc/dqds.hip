@@ -137,8 +137,28 @@ __global__ void __launch_bounds__(64 * NW, 2) dq_ds_kernel(Params p) {
     kloff[i] = 2u * (unsigned)(krow[i] * (int)rs + 8 * ((lane % C::CH) ^ swz<D>(krow[i])));
   }
 
+  // With document masking a chunk's liveness depends on the end of its key group's document.
+  // Lane i holds that end for key group i of the tile's key range, loaded once here, so that
+  // the issue of each step's loads does not wait on a load of the bounds (ranges of more than
+  // 64 key groups read them at the step).
+  const int nkg = 4 * (kb_hi - kb_lo + 1);
+  int kend_l = T;
+  if constexpr (DOC) {
+    const int kc = min(kb_lo * dsb::KEYS + 32 * lane + 31, T - 1);
+    if (lane < nkg) kend_l = p.bounds[2 * ((size_t)b * T + kc) + 1];
+  }
   auto live = [&](int st, int w) {
     const int kw = (kb_lo + (st >> 1)) * dsb::KEYS + 32 * w;
+    if constexpr (DOC) {
+      if (nkg <= 64) {
+        if (kw >= T) return false;
+        const int kc = min(kw + 31, T - 1);
+        const int kend = __builtin_amdgcn_readlane(kend_l, 4 * (st >> 1) + w);
+        const int whi1 = min(kc + W - 1, kend - 1);
+        const int qm = q0 + 32 * wave;
+        return !(qm + 31 < kw || qm > whi1);
+      }
+    }
     return dsb::chunk_live<DOC>(p.bounds, b, T, W, kw, q0 + 32 * wave);
   };
 
