@@ -105,7 +105,11 @@ __global__ void __launch_bounds__(64 * NW, 2) dq_ds_kernel(Params p) {
   const int q0 = qt * BM;
   const int myq = q0 + 32 * wave + l32;
 
-  const int kb_lo = max(0, qt - p.nslot + 1);
+  // Key blocks the tile's queries can see: the window's, and with document masking none before
+  // the block holding the document start of the tile's first query (later queries start their
+  // documents no earlier).
+  int kb_lo = max(0, qt - p.nslot + 1);
+  if constexpr (DOC) kb_lo = max(kb_lo, p.bounds[2 * ((size_t)b * T + q0)] / dsb::KEYS);
   const int kb_hi = min(qt, p.nkb - 1);
   const int nsteps = 2 * (kb_hi - kb_lo + 1);
 
