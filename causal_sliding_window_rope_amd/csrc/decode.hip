@@ -10,7 +10,10 @@
 // runs on the vector ALUs, not on MFMA: a row group of D*size/16 lanes reads one K or V row
 // with one 16-byte load per lane (the whole row in one coalesced access), keeps an online
 // softmax in exp2 units, and the window is split over several workgroups per (b, h) so that a
-// step launches ~1000 workgroups (flash-decoding); a second kernel merges the splits.
+// step launches ~768 workgroups of eight waves (flash-decoding); a second kernel merges the
+// splits. On the d24 decoding step (32 sequences, 12 heads, windows 1024 / 2048) eight-wave
+// workgroups at ~768 per step measured best among 4, 8 and 16 waves at 384 to 1024 workgroups
+// (spread ~8 %), and nontemporal cache loads another ~8 % over ordinary ones.
 #include <algorithm>
 
 #include "common.h"
@@ -91,9 +94,8 @@ __device__ __forceinline__ void merge(float& m, float& l, float* acc, float m2, 
   m = mn;
 }
 
-template <typename E, int D>
-__device__ __forceinline__ void load16(const E* src, float* dst) {
-  const uint4 w = *reinterpret_cast<const uint4*>(src);
+template <typename E>
+__device__ __forceinline__ void unpack16(const uint4 w, float* dst) {
   if constexpr (sizeof(E) == 2) {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -104,15 +106,35 @@ __device__ __forceinline__ void load16(const E* src, float* dst) {
   }
 }
 
-// one workgroup of 4 waves per (b, h, split); row group g of a wave handles every
-// (4 * RPW)-th position of the split, U positions per trip: all their loads first, then the U
+// Cached K / V rows are read once per step and not again before the other layers have swept
+// the caches through: loaded with the nontemporal hint.
+__device__ __forceinline__ uint4 ld16_stream(const void* src) {
+  const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <typename E, int D>
+__device__ __forceinline__ void load16(const E* src, float* dst) {
+  unpack16<E>(*reinterpret_cast<const uint4*>(src), dst);
+}
+
+#ifndef SWA_DECODE_WAVES
+#define SWA_DECODE_WAVES 8   // waves per workgroup (4, 8 or 16)
+#endif
+#ifndef SWA_DECODE_WG
+#define SWA_DECODE_WG 768    // workgroups per step the split count aims for
+#endif
+constexpr int NWV = SWA_DECODE_WAVES;   // waves per workgroup
+
+// one workgroup of NWV waves per (b, h, split); row group g of a wave handles every
+// (NWV * RPW)-th position of the split, U positions per trip: all their loads first, then the U
 // scores, then one online-softmax update for the U rows (rows past the split end, re-reading
 // the last one, get score -inf and weight 0, without a branch)
 template <typename E, int D>
-__global__ void __launch_bounds__(256) decode_kernel(Params p) {
+__global__ void __launch_bounds__(64 * NWV) decode_kernel(Params p) {
   using C = Cfg<E, D>;
   constexpr int VPL = C::VPL, LPR = C::LPR, RPW = C::RPW, U = C::U;
-  __shared__ float sm[4][LPR][VPL + 2];
+  __shared__ float sm[NWV][LPR][VPL + 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = blockIdx.x % p.nsplit, bh = blockIdx.x / p.nsplit;
   const int b = bh / p.H, h = bh - b * p.H;
@@ -136,7 +158,7 @@ __global__ void __launch_bounds__(256) decode_kernel(Params p) {
   for (int i = 0; i < VPL; ++i) acc[i] = 0.f;
   const size_t rs = (size_t)p.H * D;
   const size_t base = ((size_t)b * p.cap * p.H + h) * D + li * VPL;
-  constexpr int STRIDE = 4 * RPW;   // positions between a group's consecutive rows
+  constexpr int STRIDE = NWV * RPW;   // positions between a group's consecutive rows
   // trip bound uniform over the wave (the groups' last trips may hold only invalid rows)
   for (int w0 = s0 + wave * RPW; w0 < s1; w0 += STRIDE * U) {
     const int j0 = w0 + g;
@@ -145,8 +167,8 @@ __global__ void __launch_bounds__(256) decode_kernel(Params p) {
     for (int u = 0; u < U; ++u) {
       const int j = min(j0 + u * STRIDE, s1 - 1);   // past-the-end rows re-read the last one
       const size_t off = base + (size_t)(j % p.cap) * rs;
-      load16<E, D>(kc + off, kv[u]);
-      load16<E, D>(vc + off, vv[u]);
+      unpack16<E>(ld16_stream(kc + off), kv[u]);
+      unpack16<E>(ld16_stream(vc + off), vv[u]);
     }
     float d[U];
 #pragma unroll
@@ -174,7 +196,7 @@ __global__ void __launch_bounds__(256) decode_kernel(Params p) {
     }
     m = mn;
   }
-  // merge the row groups of the wave (lanes li, li + LPR, ...), then the four waves via LDS
+  // merge the row groups of the wave (lanes li, li + LPR, ...), then the waves via LDS
 #pragma unroll
   for (int msk = LPR; msk < 64; msk <<= 1) {
     float a2[VPL];
@@ -191,7 +213,7 @@ __global__ void __launch_bounds__(256) decode_kernel(Params p) {
   }
   __syncthreads();
   if (wave != 0 || g != 0) return;
-  for (int w = 1; w < 4; ++w) merge(m, l, acc, sm[w][li][VPL], sm[w][li][VPL + 1], sm[w][li], VPL);
+  for (int w = 1; w < NWV; ++w) merge(m, l, acc, sm[w][li][VPL], sm[w][li][VPL + 1], sm[w][li], VPL);
   if (p.nsplit == 1) {
     const float inv = 1.f / l;
     E* o = reinterpret_cast<E*>(p.o) + (size_t)bh * D + li * VPL;
@@ -206,22 +228,34 @@ __global__ void __launch_bounds__(256) decode_kernel(Params p) {
   }
 }
 
-// merge the splits of each (b, h): one wave per (b, h), lane owns dims lane, lane + 64
+// merge the splits of each (b, h): one wave per (b, h). Lane s holds split s's running max and
+// sum (at most 64 splits), the wave reduces them, and each lane then accumulates dims lane,
+// lane + 64 over the splits with the split weights read from their lanes; the loads of the
+// splits do not depend on one another, so several are in flight at once.
 template <typename E, int D>
 __global__ void __launch_bounds__(64) combine_kernel(Params p) {
-  const int bh = blockIdx.x, lane = threadIdx.x;
-  const float* pr = p.part + (size_t)bh * p.nsplit * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, pr[s * (D + 2) + D]);
-  float L = 0.f, acc[D / 64];
+  const int bh = blockIdx.x, lane = threadIdx.x, ns = p.nsplit;
+  const float* pr = p.part + (size_t)bh * ns * (D + 2);
+  float ms = -INFINITY, ls = 0.f;
+  if (lane < ns) {
+    ms = pr[lane * (D + 2) + D];
+    ls = pr[lane * (D + 2) + D + 1];
+  }
+  float M = ms;
+#pragma unroll
+  for (int k = 32; k > 0; k >>= 1) M = fmaxf(M, xor_shfl(M, k));
+  const float w = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+  float L = w * ls;
+#pragma unroll
+  for (int k = 32; k > 0; k >>= 1) L += xor_shfl(L, k);
+  float acc[D / 64];
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) acc[i] = 0.f;
-  for (int s = 0; s < p.nsplit; ++s) {
-    const float ms = pr[s * (D + 2) + D];
-    const float w = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-    L = fmaf(w, pr[s * (D + 2) + D + 1], L);
+#pragma unroll 8
+  for (int s = 0; s < ns; ++s) {
+    const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s));
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) acc[i] = fmaf(w, pr[s * (D + 2) + lane + 64 * i], acc[i]);
+    for (int i = 0; i < D / 64; ++i) acc[i] = fmaf(ws, pr[s * (D + 2) + lane + 64 * i], acc[i]);
   }
   E* o = reinterpret_cast<E*>(p.o) + (size_t)bh * D;
 #pragma unroll
@@ -231,10 +265,11 @@ __global__ void __launch_bounds__(64) combine_kernel(Params p) {
 
 }  // namespace dec
 
-// Splits per (b, h): about 1024 workgroups per step, at least 64 window positions per split.
+// Splits per (b, h): about SWA_DECODE_WG workgroups per step, at least 64 window positions per
+// split.
 int decode_splits(int B, int H, int window) {
   const long bh = (long)B * H;
-  int ns = (int)std::min<long>(32, std::max<long>(1, (1024 + bh - 1) / bh));
+  int ns = (int)std::min<long>(32, std::max<long>(1, (SWA_DECODE_WG + bh - 1) / bh));
   ns = std::min(ns, std::max(1, window / 64));
   return ns;
 }
@@ -266,7 +301,7 @@ hipError_t launch_decode(const void* qn, const void* kc, const void* vc, const i
   p.H = H; p.cap = cap; p.window = window;
   p.nsplit = decode_splits(B, H, window);
   p.c = scale * kLog2e;
-  const dim3 grid(B * H * p.nsplit), blk(256), cgrid(B * H), cblk(64);
+  const dim3 grid(B * H * p.nsplit), blk(64 * dec::NWV), cgrid(B * H), cblk(64);
 #define SWA_DEC(E, DD)                                                               \
   do {                                                                               \
     hipLaunchKernelGGL((dec::decode_kernel<E, DD>), grid, blk, 0, s, p);             \

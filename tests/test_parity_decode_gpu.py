@@ -54,6 +54,11 @@ CASES = [  # B, H, D, cap, W, positions, dtype
     (2, 2, 64, 300, 300, [1000, 150], "bf16"),
     (2, 3, 64, 50, 17, [3, 120], "f32"),
     (2, 2, 128, 2048, 2048, [2047, 10], "f32"),
+    (2, 12, 64, 300, 256, [299, 600], "bf16"),       # all-heads kernel, second load half used
+    (2, 16, 128, 200, 128, [150, 7], "bf16"),        # all-heads kernel, four loads per row
+    (2, 12, 128, 128, 128, [127, 300], "f32"),       # row of six loads: per-head kernel
+    # the d24 decoding step's shape (32 sequences, 12 heads, window 1024 of a 2048-slot ring)
+    (32, 12, 128, 2048, 1024, [2047] * 24 + [1023, 1024, 3000, 4095, 0, 15, 16, 17], "bf16"),
 ]
 
 
