@@ -18,12 +18,16 @@
 
 #include "common.h"
 #include "internal.h"
+#include "rope_row.h"
 
 namespace swa {
 namespace dec {
 
 // ---------------------------------------------------------------------------------------------
-// Prologue: one 64-lane wave per (b, h); lane i < D/2 owns the RoPE pair (i, i + D/2).
+// Prologue: RoPE at position pos[b], then the RMS QK-norm, of each new q and k row, in the row
+// layout of rope_row.h (TPR = D*size/16 lanes per row, 64/TPR rows per 64-lane workgroup), so
+// that the rows are bitwise what rope_qknorm_fwd computes for the same position; k and v go to
+// the cache.
 // ---------------------------------------------------------------------------------------------
 template <typename E, int D>
 __global__ void __launch_bounds__(64) prologue_kernel(const E* __restrict__ q,
@@ -33,38 +37,33 @@ __global__ void __launch_bounds__(64) prologue_kernel(const E* __restrict__ q,
                                                       const int* __restrict__ pos,
                                                       E* __restrict__ qn, E* __restrict__ kc,
                                                       E* __restrict__ vc, int H, int cap,
-                                                      float eps) {
-  constexpr int HALF = D / 2;
-  const int bh = blockIdx.x, b = bh / H, h = bh - b * H, lane = threadIdx.x;
+                                                      float eps, int nbh) {
+  using RW = RowWord<E>;
+  constexpr int VPT = RW::VPT, TPR = D / VPT, RPW = 64 / TPR;
+  const int lane = threadIdx.x, li = lane % TPR;
+  const int bh = blockIdx.x * RPW + lane / TPR;
+  if (bh >= nbh) return;   // whole row groups leave together
+  const int b = bh / H, h = bh - b * H;
   const int p = pos[b];
   const bool ok = p >= 0 && p < rows;   // the angle table must cover the position
-  const size_t in = (size_t)bh * D;
-  const size_t cr = (((size_t)b * cap + (ok ? p % cap : 0)) * H + h) * D;
-  float c = 0.f, s = 0.f;
-  if (ok && lane < HALF) {
-    c = cs[((size_t)p * HALF + lane) * 2];
-    s = cs[((size_t)p * HALF + lane) * 2 + 1];
-  }
-  auto rotate_norm = [&](const E* x, E* out) {
-    float u1 = 0.f, u2 = 0.f;
-    if (lane < HALF) {
-      const float x1 = Elem<E>::to_f(x[in + lane]), x2 = Elem<E>::to_f(x[in + lane + HALF]);
-      u1 = x1 * c - x2 * s;
-      u2 = x1 * s + x2 * c;
-    }
-    float ss = u1 * u1 + u2 * u2;
+  const size_t in = (size_t)bh * D + li * VPT;
+  float c[VPT], sn[VPT];
+  load_cs<VPT>(cs, ok ? p : 0, D / 2, (li % (TPR / 2)) * VPT, c, sn);
+  const bool second = li >= TPR / 2;
+  RW x, y;
+  x.load(q + in);
+  rope_norm_row<VPT, TPR, D>(x.v, c, sn, second, eps, y.v);
+  if (!ok) {
 #pragma unroll
-    for (int m = 32; m > 0; m >>= 1) ss += xor_shfl(ss, m);
-    const float r = 1.0f / sqrtf(ss / D + eps);
-    if (lane < HALF) {
-      out[lane] = Elem<E>::from_f(ok ? u1 * r : NAN);
-      out[lane + HALF] = Elem<E>::from_f(ok ? u2 * r : NAN);
-    }
-  };
-  rotate_norm(q, qn + in);
+    for (int e = 0; e < VPT; ++e) y.v[e] = NAN;
+  }
+  y.store(qn + in);
   if (!ok) return;   // the cache is left untouched for an invalid position
-  rotate_norm(k, kc + cr);
-  for (int d = lane; d < D; d += 64) vc[cr + d] = v[in + d];
+  const size_t cr = (((size_t)b * cap + p % cap) * H + h) * D + li * VPT;
+  x.load(k + in);
+  rope_norm_row<VPT, TPR, D>(x.v, c, sn, second, eps, y.v);
+  y.store(kc + cr);
+  *reinterpret_cast<uint4*>(vc + cr) = *reinterpret_cast<const uint4*>(v + in);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -282,10 +281,11 @@ size_t decode_workspace_bytes(int B, int H, int D, int window) {
 hipError_t launch_decode_prologue(const void* q, const void* k, const void* v, const float* cs,
                                   int rows, const int* pos, void* qn, void* kc, void* vc, int B,
                                   int H, int D, int cap, float eps, bool is_bf16, hipStream_t s) {
-  const dim3 grid(B * H), blk(64);
+  const int tpr = D * (is_bf16 ? 2 : 4) / 16, rpw = 64 / tpr;   // lanes per row, rows per wave
+  const dim3 grid((B * H + rpw - 1) / rpw), blk(64);
 #define SWA_DEC_PRO(E, DD)                                                                      \
   hipLaunchKernelGGL((dec::prologue_kernel<E, DD>), grid, blk, 0, s, (const E*)q, (const E*)k, \
-                     (const E*)v, cs, rows, pos, (E*)qn, (E*)kc, (E*)vc, H, cap, eps)
+                     (const E*)v, cs, rows, pos, (E*)qn, (E*)kc, (E*)vc, H, cap, eps, B * H)
   if (is_bf16) { if (D == 64) SWA_DEC_PRO(bf16, 64); else SWA_DEC_PRO(bf16, 128); }
   else { if (D == 64) SWA_DEC_PRO(float, 64); else SWA_DEC_PRO(float, 128); }
 #undef SWA_DEC_PRO

@@ -1,7 +1,8 @@
 """GPU parity of sliding-window decoding from a ring K/V cache against the oracle, through the
-C ABI: the positional prologue and its cache writes, the attention over the cached window
-(with and without ring wrap, with one and with several splits of the window), the agreement
-of a decoding step with the training forward's row, and invalid positions."""
+C ABI: the positional prologue and its cache writes (bitwise the training prologue's rows),
+the attention over the cached window (with and without ring wrap, with one and with several
+splits of the window), the agreement of a decoding step with the training forward's row, and
+invalid positions."""
 
 import numpy as np
 import pytest
@@ -122,3 +123,32 @@ def test_decode_invalid_positions():
     o, lse = sw.swa_decode(x, kc, vc, torch.tensor([-5, 3, 4], dtype=torch.int32, device="cuda"), 8)
     torch.cuda.synchronize()
     assert torch.isnan(o[0].float()).all() and torch.isfinite(o[1:].float()).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_prologue_matches_training_prologue(dtype, D):
+    """The decode prologue's q-hat and k-hat rows are bitwise rope_qknorm_fwd's rows at the same
+    positions (a decoding step is row p of the training forward)."""
+    B, H, T, cap = 4, 3, 40, 64
+    announce("decode prologue vs training prologue", dtype, D)
+    rng = np.random.default_rng(100 + D)
+    q, k, v = (rng.standard_normal((B, H, D)) for _ in range(3))
+    pos = np.array([0, 17, 39, 5], dtype=np.int32)
+    cs = sw.rope_table(T, D, 10000.0)
+    tq, tk, tv = dev(q, dtype), dev(k, dtype), dev(v, dtype)
+    kc = torch.zeros((B, cap, H, D), dtype=tq.dtype, device="cuda")
+    vc = torch.zeros_like(kc)
+    qn = sw.swa_decode_prologue(tq, tk, tv, cs, torch.from_numpy(pos).cuda(), kc, vc)
+    xq = torch.zeros((B, T, H, D), dtype=tq.dtype, device="cuda")
+    xk = torch.zeros_like(xq)
+    for b in range(B):
+        xq[b, pos[b]] = tq[b]
+        xk[b, pos[b]] = tk[b]
+    tqn, tkn = sw.rope_qknorm_fwd(xq, xk, cs)
+    torch.cuda.synchronize()
+    for b in range(B):
+        assert torch.equal(qn[b], tqn[b, pos[b]])
+        assert torch.equal(kc[b, pos[b] % cap], tkn[b, pos[b]])
+        assert torch.equal(vc[b, pos[b] % cap], tv[b])
+
