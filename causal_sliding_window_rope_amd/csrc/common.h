@@ -147,10 +147,23 @@ template <> __device__ __forceinline__ int swz<64>(int r) { return (((r >> 1) & 
 // Block (bh, r) of a grid of nper blocks per head in longest-first order (lpt_order in
 // internal.h): workgroup ids go to the eight XCDs in turn; XCD x holds heads x * hpx .. + hpx - 1
 // and issues rank r = 0 (a head's largest block) of each of them before rank 1.
-__device__ __forceinline__ int2 lpt_block(int nper) {
-  const int hpx = (int)(gridDim.x >> 3) / nper, j = (int)(blockIdx.x >> 3), r = j / hpx;
+// snake > 0 (kernels whose whole grid is resident at once, so that the order fixes which blocks
+// share a CU): every other round of `snake` workgroups of an XCD (one per CU) is issued in
+// reverse, so that the CUs that took the largest blocks of one round take the smallest of the
+// next.
+__device__ __forceinline__ int2 lpt_block(int nper, int snake = 0) {
+  const int hpx = (int)(gridDim.x >> 3) / nper;
+  int j = (int)(blockIdx.x >> 3);
+  if (snake > 0) {
+    const int rd = j / snake, c = j - rd * snake;
+    if ((rd & 1) && (rd + 1) * snake <= hpx * nper) j = rd * snake + (snake - 1 - c);
+  }
+  const int r = j / hpx;
   return make_int2((int)(blockIdx.x & 7) * hpx + (j - r * hpx), r);
 }
+
+// CUs per XCD of gfx950 (256 CUs in 8 XCDs).
+constexpr int kCusPerXcd = 32;
 
 // Scheduling fence: the compiler may not move instructions across it. Used to bound how far
 // ahead LDS loads are hoisted (each hoisted load keeps its result registers live).

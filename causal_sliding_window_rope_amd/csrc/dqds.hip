@@ -86,7 +86,7 @@ __global__ void __launch_bounds__(64 * NW, 2) dq_ds_kernel(Params p) {
   // written last (still in the memory-side cache) are read first.
   int bh, qt;
   if (p.lpt) {   // small full-causal grids: longest first across heads
-    const int2 br = lpt_block(p.nqt);
+    const int2 br = lpt_block(p.nqt, kCusPerXcd);
     bh = br.x;
     qt = p.nqt - 1 - br.y;
   } else {

@@ -260,7 +260,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(Params p) {
   // XCD-aware, longest-first block order.
   int bh, qb;
   if (p.lpt) {
-    const int2 br = lpt_block(p.nqb);
+    const int2 br = lpt_block(p.nqb, kCusPerXcd);
     bh = br.x;
     qb = p.nqb - 1 - br.y;
   } else {
