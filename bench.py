@@ -159,14 +159,15 @@ def run_bench(args):
             raise sw.SwaError(name, st, lib.swa_last_error().decode())
 
     fused_gate = args.fused_gate
-    # the query half of the prologue inside swa_fwd_qnorm / swa_bwd_dq_ds_qnorm (stored-dS
-    # backward only); the prologue calls then run on k alone. By default where it is measured
-    # faster: at head dim 128 (the d24 layers); at 64 (the GPT-2 layer) each forward workgroup's
-    # prologue loads are a larger share of its short key range and the separate pass wins.
-    if args.qnorm == "auto":
-        qnorm = stored_ds and not args.no_qnorm and D == 128
-    else:
-        qnorm = stored_ds and not args.no_qnorm and args.qnorm == "on"
+    # the query half of the prologue inside swa_fwd_qnorm and / or its backward inside
+    # swa_bwd_dq_ds_qnorm (stored-dS backward only); the prologue calls then run on k alone for
+    # that half. By default both (measured fastest or level on the d24 sweep and the GPT-2
+    # layer).
+    mode = "off" if args.no_qnorm else args.qnorm
+    if mode == "auto":
+        mode = "on"
+    qn_fwd = stored_ds and mode in ("on", "fwd")   # the forward half inside swa_fwd_qnorm
+    qn_bwd = stored_ds and mode in ("on", "bwd")   # its backward inside swa_bwd_dq_ds_qnorm
 
     def step(rec):
         stream = sw._stream()   # the current stream: the capture stream when recording a graph
@@ -174,8 +175,8 @@ def run_bench(args):
         for li, t in enumerate(layers):
             bounds, ids = t.get("bounds"), t.get("ids")
             rows = 0 if ids is None else t["ve"].shape[0]
-            call("rope_qknorm_fwd", None if qnorm else P(t["q"]), P(t["k"]), P(cs),
-                 None if qnorm else P(t["qn"]), P(t["kn"]), B, T, H, D, 1e-6, sw.SWA_BF16, stream)
+            call("rope_qknorm_fwd", None if qn_fwd else P(t["q"]), P(t["k"]), P(cs),
+                 None if qn_fwd else P(t["qn"]), P(t["kn"]), B, T, H, D, 1e-6, sw.SWA_BF16, stream)
             ve = gate = fids = None
             frows, v = 0, t["v"]
             if cfg["gate"] and fused_gate:
@@ -187,7 +188,7 @@ def run_bench(args):
                      P(ids), rows, P(t["veff"]), B, T, H, D, sw.SWA_BF16, stream)
                 v = t["veff"]
             if rec: rec["fwd"][li][0].record()
-            if qnorm:
+            if qn_fwd:
                 call("swa_fwd_qnorm", P(t["q"]), P(cs), 1e-6, P(t["kn"]), P(v), P(ve), P(gate),
                      P(fids), frows, P(bounds), P(t["qn"]), P(t["o"]), P(t["lse"]),
                      B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
@@ -219,7 +220,7 @@ def run_bench(args):
                      frows, P(bounds), P(t["lse"]), P(t["dO"]), P(g["dkn"]), P(g["dv"]), P(dve),
                      P(dgate), P(ws), nws, B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
                 if rec: rec["bwd"][li][2].record()
-                if qnorm:   # dq w.r.t. the raw q straight from the dQ kernel
+                if qn_bwd:   # dq w.r.t. the raw q straight from the dQ kernel
                     call("swa_bwd_dq_ds_qnorm", P(t["kn"]), P(bounds), P(t["q"]), P(cs), 1e-6,
                          P(g["dq"]), P(ws), nws, B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
                 else:
@@ -239,8 +240,8 @@ def run_bench(args):
                      P(t["dO"]), P(g["dkn"]), P(g["dv"]), P(dve), P(dgate), P(ws), nws,
                      B, T, H, D, t["W"], scale, sw.SWA_BF16, stream)
                 if rec: rec["bwd"][li][3].record()
-            call("rope_qknorm_bwd", None if qnorm else P(t["q"]), P(t["k"]), P(cs),
-                 None if qnorm else P(g["dqn"]), P(g["dkn"]), None if qnorm else P(g["dq"]),
+            call("rope_qknorm_bwd", None if qn_bwd else P(t["q"]), P(t["k"]), P(cs),
+                 None if qn_bwd else P(g["dqn"]), P(g["dkn"]), None if qn_bwd else P(g["dq"]),
                  P(g["dk"]), B, T, H, D, 1e-6, sw.SWA_BF16, stream)
             if cfg["gate"]:
                 if not fused_gate:   # dve, dgate from dv_eff (= dv)
@@ -349,8 +350,14 @@ def run_bench(args):
             "swa_bwd_tflops_credited": round(bwd_tf, 2),
             "backward": ("row terms, dK/dV storing dS, dQ from the stored dS" if stored_ds
                          else "dQ with the row terms, then dK/dV (S and dP recomputed twice)"),
-            "query_prologue": ("inside the forward and dQ kernels (their times include it)"
-                               if qnorm else "in the prologue calls"),
+            "query_prologue": {("on", "on"): "inside the forward and dQ kernels (their times "
+                                              "include it)",
+                               ("on", "off"): "forward inside the forward kernel, backward in "
+                                              "the prologue call",
+                               ("off", "on"): "forward in the prologue call, backward inside "
+                                              "the dQ kernel",
+                               ("off", "off"): "in the prologue calls"}[
+                                   ("on" if qn_fwd else "off", "on" if qn_bwd else "off")],
             "swa_bwd_dkdv_tflops_executed": round(kv_flop / (kv_ms / args.steps * 1e-3) / 1e12, 2),
             "swa_bwd_dq_tflops_executed": round(dq_flop / (dq_ms / args.steps * 1e-3) / 1e12, 2),
             "swa_fwd_ms_per_step": round(fwd_ms / args.steps, 4),
@@ -733,11 +740,12 @@ def main():
     ap.add_argument("--bwd", choices=("ds", "recompute"), default="ds",
                     help="backward: dS stored by the dK/dV kernel and read by the dQ kernel "
                          "(default), or S and dP recomputed in both")
-    ap.add_argument("--qnorm", choices=("auto", "on", "off"), default="auto",
-                    help="with --bwd ds: run the query half of the RoPE/QK-norm prologue (and of "
-                         "its backward) inside the forward and dQ kernels (swa_fwd_qnorm, "
-                         "swa_bwd_dq_ds_qnorm: on) or in the separate prologue calls (off); auto: "
-                         "on at head dim 128, off at 64")
+    ap.add_argument("--qnorm", choices=("auto", "on", "off", "fwd", "bwd"), default="auto",
+                    help="with --bwd ds: run the query half of the RoPE/QK-norm prologue and of "
+                         "its backward inside the forward and dQ kernels (swa_fwd_qnorm, "
+                         "swa_bwd_dq_ds_qnorm: on), only the forward half (fwd) or only the "
+                         "backward half (bwd) there, or both in the separate prologue calls "
+                         "(off); auto: on")
     ap.add_argument("--no-qnorm", action="store_true", help="the same as --qnorm off")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="only run a plain device-to-device copy of this many MiB 5 times (used to "
