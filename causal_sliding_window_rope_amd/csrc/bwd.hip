@@ -75,7 +75,11 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const E* __restrict__ o,
   for (int i = 0; i < PASSES; ++i) {
     const int t = min(t0 + i * RPP + rr, T - 1);
     const size_t off = (((size_t)b * T + t) * H + h) * D + lr * VPT;
-    a[i] = *reinterpret_cast<const uint4*>(o + off);
+    // O is read by no later kernel of the backward: nontemporal. dO is, by dK/dV right after.
+    {
+      const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(o + off));
+      a[i] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
     g[i] = *reinterpret_cast<const uint4*>(dO + off);
   }
 #pragma unroll
