@@ -303,7 +303,7 @@ __global__ void __launch_bounds__(64 * NW, 2) dq_ds_kernel(Params p) {
 #pragma unroll
     for (int pass = 0; pass < NP; ++pass) {
       const int t = min(q0 + pass * RPP + tid / TPR, T - 1);
-      x[pass].load(p.qraw + head0 + (size_t)t * rs + lr * VPT);
+      x[pass].load_stream(p.qraw + head0 + (size_t)t * rs + lr * VPT);
       load_cs<VPT>(p.cs, t, D / 2, (lr % (TPR / 2)) * VPT, c[pass], s[pass]);
     }
     __syncthreads();

@@ -26,6 +26,17 @@ template <typename E> struct RowWord {
       v[4] = bf_lo(w.z); v[5] = bf_hi(w.z); v[6] = bf_lo(w.w); v[7] = bf_hi(w.w);
     }
   }
+  // the same with the nontemporal hint (rows read once where they are read)
+  __device__ __forceinline__ void load_stream(const E* p) {
+    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    if constexpr (sizeof(E) == 4) {
+      v[0] = __uint_as_float(w[0]); v[1] = __uint_as_float(w[1]);
+      v[2] = __uint_as_float(w[2]); v[3] = __uint_as_float(w[3]);
+    } else {
+      v[0] = bf_lo(w[0]); v[1] = bf_hi(w[0]); v[2] = bf_lo(w[1]); v[3] = bf_hi(w[1]);
+      v[4] = bf_lo(w[2]); v[5] = bf_hi(w[2]); v[6] = bf_lo(w[3]); v[7] = bf_hi(w[3]);
+    }
+  }
   __device__ __forceinline__ void store(E* p) const {
     uint4 w;
     if constexpr (sizeof(E) == 4) {
