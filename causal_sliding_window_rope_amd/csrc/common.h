@@ -92,6 +92,36 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
+// One query row of an O^T accumulator tile (32 dims x 32 queries, lane = query l32, half hi
+// holding dims 8a + 4hi .. + 3 of each group of 8, a < 4), scaled by `inv` and stored as bf16
+// at row + 32 db in 16-byte pieces: the lane stores dims 16j + 8hi .. + 7 of each 16 (a = 2j + hi)
+// and takes the other four from its partner lane (same query) by a half-wave swap. Every lane
+// of the wave takes part in the swap; `store` gates the memory write.
+template <typename V16>
+__device__ __forceinline__ void store_orow16(bf16* row, int db, const V16& acc, float inv,
+                                             int hi, bool store) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    unsigned c[2][2];   // this lane's 4 dims of a = 2j and of a = 2j + 1, as bf16 pairs
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int a = 2 * j + e;
+      c[e][0] = pack_bf2(acc[4 * a + 0] * inv, acc[4 * a + 1] * inv);
+      c[e][1] = pack_bf2(acc[4 * a + 2] * inv, acc[4 * a + 3] * inv);
+    }
+    unsigned r[2];   // the partner's 4 dims of this lane's a
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const unsigned sv = hi ? c[0][x] : c[1][x];
+      const auto pr = __builtin_amdgcn_permlane32_swap(sv, sv, false, false);
+      r[x] = hi ? pr[0] : pr[1];
+    }
+    const u32x4 w = hi ? (u32x4){r[0], r[1], c[1][0], c[1][1]}
+                       : (u32x4){c[0][0], c[0][1], r[0], r[1]};
+    if (store) *reinterpret_cast<u32x4*>(row + 32 * db + 16 * j + 8 * hi) = w;
+  }
+}
+
 // Asynchronous 16-byte global -> LDS copy in its buffer form (buffer_load_dwordx4 ... lds):
 // lane l of the wave reads resource + voff bytes and writes lds_base + 16*l bytes (lds_base
 // must be the same for the whole wave). The resource is a uniform base address with a range of

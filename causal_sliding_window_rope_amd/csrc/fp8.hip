@@ -296,19 +296,11 @@ __global__ void __launch_bounds__(64 * NW, 3) fwd_fp8_kernel(Params p) {
 
   const float l_tot = ws.l_run + half_swap(ws.l_run);
   const float inv = p.vscale / l_tot;
-  if (myq < T) {
-    bf16* op = p.o + head0 + (size_t)myq * H * D;
+  bf16* op = p.o + head0 + (size_t)min(myq, T - 1) * H * D;
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        uint2 w;
-        w.x = pack_bf2(ws.oacc[db][4 * a + 0] * inv, ws.oacc[db][4 * a + 1] * inv);
-        w.y = pack_bf2(ws.oacc[db][4 * a + 2] * inv, ws.oacc[db][4 * a + 3] * inv);
-        *reinterpret_cast<uint2*>(op + db * 32 + 8 * a + 4 * hi) = w;
-      }
-    if (hi == 0) p.lse[((size_t)b * H + h) * T + myq] = (ws.m_ref + __log2f(l_tot)) * kLn2;
-  }
+  for (int db = 0; db < C::NDB; ++db) store_orow16(op, db, ws.oacc[db], inv, hi, myq < T);
+  if (myq < T && hi == 0)
+    p.lse[((size_t)b * H + h) * T + myq] = (ws.m_ref + __log2f(l_tot)) * kLn2;
 }
 
 }  // namespace f8k
