@@ -10,12 +10,13 @@
 //
 // One workgroup = 4 waves = one 128-query tile of one (b, h); wave w owns queries 32 w .. +31,
 // which is unit w of every chunk, so a wave reads only its own chunks. Steps of 64 keys (half a
-// key block: key groups 2h, 2h + 1), issued PF = 3 steps ahead of the one computed: the wave's
-// two chunks of a step go straight into registers (one 16-byte load per lane per half chunk),
-// the K rows (row-major, 16-byte chunks XOR-swizzled) into a ring of RING = 4 LDS slots by
-// asynchronous global->LDS copies. Streaming dS from HBM is what bounds this kernel: with
-// two-stage LDS buffering of both it reached about 3.4 TB/s, too few bytes in flight per CU;
-// registers hold three steps of dS per wave without taking LDS. At its step, a wave writes its
+// key block: key groups 2h, 2h + 1). The wave's two chunks of a step go straight into registers
+// (one 16-byte load per lane per half chunk), PF steps ahead of the one computed, and its share
+// of the step's K rows (row-major, 16-byte chunks XOR-swizzled) into registers KPF steps ahead,
+// written into one of two LDS buffers at the step (Pipe below). Streaming dS from HBM is what
+// bounds this kernel: with two-stage LDS buffering of both it reached about 3.4 TB/s, too few
+// bytes in flight per CU; registers hold several steps of dS per wave without taking LDS, or,
+// with three workgroups per CU, more waves hold one step each. At its step, a wave writes its
 // chunks into a private LDS buffer and reads them back transposed. dQ^T += K^T dS^T on
 // v_mfma_f32_32x32x16_bf16: A = K^T by transposing LDS reads of the K rows, B = dS^T by
 // transposing reads of the chunk (lane = query, 4 keys per read), both in natural key order.
@@ -32,10 +33,19 @@ namespace dqs {
 constexpr int NW = 4;
 constexpr int BM = dsb::QUERIES;   // queries per workgroup
 constexpr int BN = 64;             // keys per step
-constexpr int PF = 3;              // dS: steps issued ahead of the one computed
-constexpr int RING = PF + 1;       // dS register sets
-constexpr int KPF = 2;             // K: steps issued ahead
-constexpr int UNROLL = 2 * RING;   // steps per loop trip (a multiple of RING and of KPF)
+// Load pipeline. Without document masking: two workgroups per CU, dS issued PF = 3 and K KPF = 2
+// steps ahead. With document masking the workgroups' lengths follow the documents, and three
+// workgroups per CU (<= 168 VGPRs: dS and K one step ahead, the epilogue's row loads in two
+// batches) measured 15 % faster on the masked d24 layer (193 -> 164 us); without masking the
+// same configuration was level on the d24 sweep and slower on the GPT-2 layer.
+template <bool DOC> struct Pipe {
+  static constexpr int PF = DOC ? 1 : 3;         // dS: steps issued ahead of the one computed
+  static constexpr int RING = PF + 1;            // dS register sets
+  static constexpr int KPF = DOC ? 1 : 2;        // K: steps issued ahead
+  static constexpr int UNROLL = 2 * RING;        // steps per loop trip (a multiple of RING and KPF)
+  static constexpr int WG_PER_CU = DOC ? 3 : 2;
+  static constexpr int NBATCH = DOC ? 2 : 1;     // batches of the query-prologue epilogue's loads
+};
 
 template <int D> struct Cfg {
   static constexpr int CH = D / 8;            // 16-byte chunks per K row
@@ -64,8 +74,10 @@ __device__ __forceinline__ void ds_store_b128(lds_t<char>* p, u32x4 v) {
 }
 
 template <int D, bool DOC, bool QN>
-__global__ void __launch_bounds__(64 * NW, 2) dq_ds_kernel(Params p) {
+__global__ void __launch_bounds__(64 * NW, Pipe<DOC>::WG_PER_CU) dq_ds_kernel(Params p) {
   using C = Cfg<D>;
+  constexpr int PF = Pipe<DOC>::PF, RING = Pipe<DOC>::RING, KPF = Pipe<DOC>::KPF,
+                UNROLL = Pipe<DOC>::UNROLL, NBATCH = Pipe<DOC>::NBATCH;
   constexpr int NDB = D / 32;
   // K tiles: double-buffered, written from registers at their step. Transpose buffers: each
   // wave's two stored chunks of the current step (written from registers).
@@ -296,16 +308,22 @@ __global__ void __launch_bounds__(64 * NW, 2) dq_ds_kernel(Params p) {
     constexpr int VPT = RW::VPT, TPR = D / VPT, RPP = 64 * NW / TPR, NP = BM / RPP;
     const int lr = tid % TPR;
     const bool second = lr >= TPR / 2;
-    // the raw rows and angles of every pass first (rows past the end re-read the last row and
-    // store nothing); their latency overlaps the staging below
-    RW x[NP];
-    float c[NP][VPT], s[NP][VPT];
+    // The raw rows and angles of the passes are loaded in NBATCH batches (rows past the end
+    // re-read the last row and store nothing); the first batch's latency overlaps the staging
+    // below.
+    constexpr int PB = NP / NBATCH;
+    static_assert(NP % NBATCH == 0, "whole batches");
+    RW x[PB];
+    float c[PB][VPT], s[PB][VPT];
+    auto load_batch = [&](int bt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int pass = 0; pass < NP; ++pass) {
-      const int t = min(q0 + pass * RPP + tid / TPR, T - 1);
-      x[pass].load_stream(p.qraw + head0 + (size_t)t * rs + lr * VPT);
-      load_cs<VPT>(p.cs, t, D / 2, (lr % (TPR / 2)) * VPT, c[pass], s[pass]);
-    }
+      for (int pp = 0; pp < PB; ++pp) {
+        const int t = min(q0 + (bt * PB + pp) * RPP + tid / TPR, T - 1);
+        x[pp].load_stream(p.qraw + head0 + (size_t)t * rs + lr * VPT);
+        load_cs<VPT>(p.cs, t, D / 2, (lr % (TPR / 2)) * VPT, c[pp], s[pp]);
+      }
+    };
+    load_batch(0);
     __syncthreads();
     if (myq < T) {
       const int rl = (32 * wave + l32) & 63;
@@ -322,23 +340,27 @@ __global__ void __launch_bounds__(64 * NW, 2) dq_ds_kernel(Params p) {
     }
     __syncthreads();
 #pragma unroll
-    for (int pass = 0; pass < NP; ++pass) {
-      const int r = pass * RPP + tid / TPR;
-      const int t = q0 + r;
-      const int rl = r & 63;
-      const u32x4 gw = *reinterpret_cast<const lds_t<u32x4>*>(kslot(r >> 6) + rl * D +
-                                                               8 * (lr ^ swz<D>(rl)));
-      RW g, out;
-      g.v[0] = bf_lo(gw[0]); g.v[1] = bf_hi(gw[0]); g.v[2] = bf_lo(gw[1]); g.v[3] = bf_hi(gw[1]);
-      g.v[4] = bf_lo(gw[2]); g.v[5] = bf_hi(gw[2]); g.v[6] = bf_lo(gw[3]); g.v[7] = bf_hi(gw[3]);
-      rope_norm_row_bwd<VPT, TPR, D>(x[pass].v, g.v, c[pass], s[pass], second, p.eps, out.v);
-      // dq is the layer's final output: written with the nontemporal hint, so that it does not
-      // displace cached data (~3 % of this kernel's time on the d24 sweep)
-      if (t < T) {
-        const u32x4 w = {pack_bf2(out.v[0], out.v[1]), pack_bf2(out.v[2], out.v[3]),
-                         pack_bf2(out.v[4], out.v[5]), pack_bf2(out.v[6], out.v[7])};
-        __builtin_nontemporal_store(
-            w, reinterpret_cast<u32x4*>(p.dq + head0 + (size_t)t * rs + lr * VPT));
+    for (int bt = 0; bt < NBATCH; ++bt) {
+      if (bt > 0) load_batch(bt);
+#pragma unroll
+      for (int pp = 0; pp < PB; ++pp) {
+        const int r = (bt * PB + pp) * RPP + tid / TPR;
+        const int t = q0 + r;
+        const int rl = r & 63;
+        const u32x4 gw = *reinterpret_cast<const lds_t<u32x4>*>(kslot(r >> 6) + rl * D +
+                                                                 8 * (lr ^ swz<D>(rl)));
+        RW g, out;
+        g.v[0] = bf_lo(gw[0]); g.v[1] = bf_hi(gw[0]); g.v[2] = bf_lo(gw[1]); g.v[3] = bf_hi(gw[1]);
+        g.v[4] = bf_lo(gw[2]); g.v[5] = bf_hi(gw[2]); g.v[6] = bf_lo(gw[3]); g.v[7] = bf_hi(gw[3]);
+        rope_norm_row_bwd<VPT, TPR, D>(x[pp].v, g.v, c[pp], s[pp], second, p.eps, out.v);
+        // dq is the layer's final output: written with the nontemporal hint, so that it does
+        // not displace cached data (~3 % of this kernel's time on the d24 sweep)
+        if (t < T) {
+          const u32x4 w = {pack_bf2(out.v[0], out.v[1]), pack_bf2(out.v[2], out.v[3]),
+                           pack_bf2(out.v[4], out.v[5]), pack_bf2(out.v[6], out.v[7])};
+          __builtin_nontemporal_store(
+              w, reinterpret_cast<u32x4*>(p.dq + head0 + (size_t)t * rs + lr * VPT));
+        }
       }
     }
     return;
