@@ -71,13 +71,19 @@ def test_layer_with_documents_and_gate():
     compare_layer(g, fwd, bwd, "bf16", gate=True)
 
 
-def test_full_size_documents_sampled_heads():
+@pytest.mark.parametrize("route", ["recompute", "benchmarked"])
+def test_full_size_documents_sampled_heads(route):
     """The d24 short layer (B=16, T=2048, H=12, D=128, W=1024) on packed rows with ~512-token
-    documents, in the benchmarked launch configuration; whole (b, h) heads checked."""
+    documents, whole (b, h) heads checked: on the recomputing backward with the separate
+    prologue, and on the route the benchmark times (query prologue inside the forward and dQ
+    kernels, backward with the stored score gradient)."""
     wl = WORKLOADS["d24_short_doc"]
-    announce("full size docs")
+    announce("full size docs", route)
     x = make_inputs(wl)
-    g = gpu_layer(x, wl, wl.window)
+    if route == "benchmarked":
+        g = gpu_layer(x, wl, wl.window, bwd="ds", qnorm=True)
+    else:
+        g = gpu_layer(x, wl, wl.window)
     for sel in ((0, 0), (15, 11), (7, 4)):
         fwd, bwd = oracle_layer(x, wl, wl.window, sel=sel)
         errs = compare_layer(g, fwd, bwd, wl.dtype, sel=sel)

@@ -81,9 +81,10 @@ def test_qnorm_with_fused_gate(T, W, D):
                  gate=True)
 
 
-def test_qnorm_document_masking():
-    announce("qnorm doc")
-    _both_routes(small_workload(2, 300, 2, 128, 100, "bf16", seed=1500, doc_mean=40), 100)
+@pytest.mark.parametrize("T,W,D,mean", [(300, 100, 128, 40), (700, 256, 64, 90)])
+def test_qnorm_document_masking(T, W, D, mean):
+    announce("qnorm doc", T, W, D, mean)
+    _both_routes(small_workload(2, T, 2, D, W, "bf16", seed=1500 + T, doc_mean=mean), W)
 
 
 @pytest.mark.parametrize("name", ["d24_short", "d24_full", "gpt2_124m"])
