@@ -137,12 +137,12 @@ def test_ds_ve_table():
                                         ("d24_full", [(0, 0), (15, 11)]),
                                         ("gpt2_124m", [(0, 0), (7, 11)])])
 def test_ds_full_size_sampled_heads(name, heads):
-    """Full layer in the benchmarked configuration (the stored-dS backward); the oracle checks
-    whole (b, h) heads."""
+    """Full layer on the route the benchmark times (query prologue inside the forward and dQ
+    kernels, the stored-dS backward); the oracle checks whole (b, h) heads."""
     wl = WORKLOADS[name]
     announce("ds full size", name)
     x = make_inputs(wl)
-    g = gpu_layer(x, wl, wl.window, bwd="ds")
+    g = gpu_layer(x, wl, wl.window, bwd="ds", qnorm=True)
     for sel in heads:
         fwd, bwd = oracle_layer(x, wl, wl.window, sel=sel)
         compare_layer(g, fwd, bwd, "bf16", sel=sel)

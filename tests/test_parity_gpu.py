@@ -153,8 +153,10 @@ FULL = [("gpt2_124m", [(0, 0), (7, 11), (3, 5)]),
 
 @pytest.mark.parametrize("name,heads", FULL)
 def test_full_size_sampled_heads(name, heads):
-    """Full workload on the GPU in the benchmarked launch configuration; the oracle checks
-    whole (b, h) heads (every query row and every gradient of those heads)."""
+    """Full workload on the GPU, at the benchmark's shapes, on the recomputing backward with the
+    separate prologue (the benchmarked route has its own full-size test with the stored-dS
+    backward); the oracle checks whole (b, h) heads (every query row and every gradient of those
+    heads)."""
     wl = WORKLOADS[name]
     announce("full size", name)
     x = make_inputs(wl)
