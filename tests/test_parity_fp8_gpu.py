@@ -165,3 +165,40 @@ def test_fwd_fp8_close_to_bf16_kernel():
     torch.cuda.synchronize()
     assert rel_l2(host(o8), host(o16)) <= 0.1
     assert float((l8 - l16).abs().max()) <= 0.3
+
+
+@pytest.mark.parametrize("name,heads", [("d24_short", [(0, 0), (15, 11)]),
+                                        ("d24_full", [(7, 5)])])
+def test_fwd_fp8_full_size_sampled_heads(name, heads):
+    """The route the fp8 benchmark times, at the d24 layer shapes (B=16, T=2048, H=12, D=128,
+    W = 1024 and 2048): rope_qknorm_fwd_fp8 writes q_hat, k_hat as e4m3 at scale 1,
+    swa_fp8_pack packs v at scale 1/64, swa_fwd_fp8 runs the attention. Whole (b, h) heads
+    against the oracle's own prologue, quantisation and attention from the raw inputs (the
+    kernel's float32 prologue may round a value lying within float32 distance of an e4m3
+    boundary to the other neighbour; O's bar absorbs that)."""
+    from causal_sliding_window_rope_amd.inputs import WORKLOADS
+    wl = WORKLOADS[name]
+    B, T, H, D, W = wl.B, wl.T, wl.H, wl.D, wl.window
+    announce("fp8 full size", name)
+    x = make_inputs(wl)
+    q, k, v = (dev(x[n], "bf16") for n in ("q", "k", "v"))
+    cs = sw.rope_table(T, D, wl.base)
+    q8, k8 = sw.rope_qknorm_fwd_fp8(q, k, cs, wl.eps)
+    _, _, v8t = sw.swa_fp8_pack(None, None, v, 1.0, 1.0, 1.0 / 64)
+    o, lse = sw.swa_fwd_fp8(q8, k8, v8t, W, 1.0, 1.0, 1.0 / 64)
+    torch.cuda.synchronize()
+    o, lse = host(o), host(lse)
+    for b, h in heads:
+        sl = lambda a: a[b:b + 1, :, h:h + 1, :].astype(np.float64)
+        qh = oracle.rope_qknorm(sl(x["q"]), wl.base, wl.eps)[0]
+        kh = oracle.rope_qknorm(sl(x["k"]), wl.base, wl.eps)[0]
+        want_o, want_lse = fp8.attention_fwd_fp8(fp8.quantize(qh, 1.0), fp8.quantize(kh, 1.0),
+                                                 fp8.quantize(sl(x["v"]), 1.0 / 64), 1.0, 1.0,
+                                                 1.0 / 64, W, wl.scale)
+        got_o = o[b:b + 1, :, h:h + 1, :]
+        assert np.all(np.isfinite(got_o))
+        err = rel_l2(got_o, want_o)
+        assert err <= FP8_REL_L2, f"{name} {(b, h)}: O rel L2 {err:.4g}"
+        lerr = np.max(np.abs(lse[b:b + 1, h:h + 1] - want_lse))
+        assert lerr <= BF16_LSE_ABS, f"{name} {(b, h)}: lse {lerr:.3g}"
+        print(name, (b, h), f"O {err:.3e} lse {lerr:.3e}")
