@@ -260,9 +260,10 @@ __global__ void __launch_bounds__(64 * NW, Pipe<DOC>::WG_PER_CU) dq_ds_kernel(Pa
   // Step st: write its K rows and its dS chunks into LDS (every wave is past the previous
   // step's barrier, so no wave still reads the K buffer of step st - 2), workgroup barrier,
   // load the K rows of step st + KPF and the dS chunks of step st + PF into the registers just
-  // freed, compute step st. The compiler waits for the K rows of step st; the counter being in
-  // order, that also waits for the loads issued before them, which still leaves the dS loads of
-  // steps st + 1 .. st + PF - 1 and the K rows of step st + 1 in flight.
+  // freed, compute step st. The compiler waits for the K rows and dS chunks of step st; the
+  // counter being in order, that also waits for the loads issued before them, which still leaves
+  // the dS loads of steps st + 1 .. st + PF - 1 and the K rows of steps st + 1 .. st + KPF - 1 in
+  // flight.
   auto step = [&](int st, int R) __attribute__((always_inline)) {
     put_k(kreg[R % KPF], R & 1);
     stage(dsr[R]);
@@ -284,9 +285,11 @@ __global__ void __launch_bounds__(64 * NW, Pipe<DOC>::WG_PER_CU) dq_ds_kernel(Pa
   sched_fence();
   // Unrolled by two turns of the register ring: the compiler's wait analysis does not carry
   // the ages of the ring's loads across the loop's back edge and waits for all of them at its
-  // head, so the head comes once per UNROLL steps. Each step waits for the K copy issued one
-  // step earlier and, the counter being in order, for every dS load issued before it: those of
-  // step st + PF - 2, which leaves PF - 2 steps of dS loads in flight.
+  // head, so the head comes once per UNROLL steps. Each step waits for its own K rows and dS
+  // chunks (issued KPF and PF steps earlier) and, the counter being in order, for every load
+  // issued before them: with PF = 3 the dS loads of the next step stay in flight; with PF = 1
+  // (three workgroups per CU) none of the wave's loads do, and the CU's other workgroups cover
+  // the wait.
   for (int st = 0; st < nsteps; st += UNROLL) {
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
